@@ -1,0 +1,312 @@
+"""Benchmark of the hybrid SWA / NoPE attention core on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-decode] [--no-cpu-baseline]
+
+One step = one pass of the attention hot path over the long-prefill workload: 8
+sequences, each adding 2,048 new tokens on top of 98,304 cached tokens (64-token
+pages in shuffled physical order, bf16 KV), through both layer kinds:
+  full NoPE/SSMax layer: fused Q/K norm + SSMax + KV store, then prefill attention
+                         with the fused sigmoid head gate;
+  sliding-window layer:  fused Q/K norm + RoPE + KV store, then prefill attention
+                         (window 512) with the gate.
+All inputs are seeded synthetic tensors already resident in HBM when the timed region
+starts. The printed JSON line reports new tokens per second through the step, the
+roofline of the dominant kernel (full-layer prefill, bf16 MFMA) measured with HIP
+events on its stream, per-layer figures, the decode / verify workloads (HBM roofline),
+and the fp64 CPU oracle timed on a bounded sample of the same workload.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HQ, HKV, D = 48, 8, 128
+PEAK_BF16_TFLOPS = 2500.0        # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0            # MI355X HBM3E
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def visible_pairs(q_lens, kv_lens, kind, window=512):
+    """Visible (query token, key) pairs per head, summed over sequences."""
+    total = 0
+    for n, L in zip(q_lens, kv_lens):
+        for i in range(int(n)):
+            pos = int(L) - int(n) + i
+            total += min(pos + 1, window) if kind == "swa" else pos + 1
+    return total
+
+
+def visible_keys_decode(q_lens, kv_lens, kind, window=512):
+    """Distinct keys a decode call must read per sequence (union over its new tokens)."""
+    total = 0
+    for n, L in zip(q_lens, kv_lens):
+        first = int(L) - int(n)
+        lo = max(0, first - window + 1) if kind == "swa" else 0
+        total += int(L) - lo
+    return total
+
+
+class Staged:
+    """One layer call staged on the GPU."""
+
+    def __init__(self, call, device="cuda"):
+        import torch
+        from nope_gqa_attention_amd import beamattn as ba
+        from nope_gqa_attention_amd.layer import HybridAttention
+
+        self.call = call
+        self.batch = ba.DeviceBatch(call.q_start, call.kv_len, call.block_table, device)
+        self.cache = ba.DeviceCache(call.k_cache.to(device), call.v_cache.to(device),
+                                    call.k_scale, call.v_scale)
+        self.layer = HybridAttention(call.kind)
+        for n in ("q", "k", "v", "gate", "q_norm_w", "k_norm_w", "gate_bias"):
+            setattr(self, n, getattr(call, n).to(device))
+        self.q_out = torch.empty_like(self.q)
+        self.out = torch.empty_like(self.q)
+        self.ws = self.layer.workspace(self.batch) if call.max_q_len <= 16 else None
+
+    def kvwrite(self):
+        self.layer.kvwrite(self.batch, self.cache, self.q, self.k, self.v, self.q_norm_w,
+                           self.k_norm_w, self.q_out)
+
+    def attend(self, mode):
+        self.layer.attend(self.batch, self.cache, self.q_out, self.gate, self.gate_bias, self.out,
+                          mode=mode)
+
+
+def timed_steps(parts, steps, warmup):
+    """parts: list of (name, fn). Runs warmup + steps passes; returns (total ms per step,
+    {name: mean ms per launch}) from HIP events recorded on torch's current stream, which
+    is the stream every entry point is launched on."""
+    import torch
+
+    for _ in range(warmup):
+        for _, fn in parts:
+            fn()
+    torch.cuda.synchronize()
+    ev = {name: [] for name, _ in parts}
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(steps):
+        for name, fn in parts:
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record()
+            fn()
+            b.record()
+            ev[name].append((a, b))
+    end.record()
+    torch.cuda.synchronize()
+    total = start.elapsed_time(end) / steps
+    per = {name: sum(a.elapsed_time(b) for a, b in lst) / len(lst) for name, lst in ev.items()}
+    return total, per
+
+
+def cpu_baseline(calls_host, budget_rows):
+    """Time the fp64 oracle on the host on a bounded sample of the prefill workload:
+    the last `budget_rows` new tokens of sequence 0 of each layer kind (kvwrite of the
+    sequence's new tokens, attention over its full visible context, gate)."""
+    import numpy as np
+
+    import oracle.beam_oracle as O
+
+    total_t, total_rows = 0.0, 0
+    for kind, inp, rows in calls_host:
+        t0 = time.perf_counter()
+        O.layer_call(inp, rows=rows)
+        total_t += time.perf_counter() - t0
+        total_rows += len(rows)
+    threads = None
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max((p.get("num_threads") or 0) for p in threadpool_info()) or None
+    except Exception:
+        pass
+    return total_rows, total_t, threads or os.cpu_count()
+
+
+def seq0_host_inputs(call, rows_wanted):
+    """Oracle inputs for sequence 0 of a staged call only: its pages copied to the host
+    and renumbered, so the oracle reads exactly what the GPU read."""
+    import numpy as np
+    import torch
+
+    bt = call.block_table[0]
+    pages = np.unique(bt)
+    remap = {int(p): i for i, p in enumerate(pages)}
+    idx = torch.from_numpy(pages.astype(np.int64))
+    kc = call.k_cache[idx.to(call.k_cache.device)].cpu()
+    vc = call.v_cache[idx.to(call.v_cache.device)].cpu()
+    n0 = int(call.q_start[1] - call.q_start[0])
+
+    def bits(t):
+        return t.view(torch.int16).numpy().view(np.uint16) if t.dtype == torch.bfloat16 else t.numpy()
+
+    inp = {
+        "kind": call.kind, "kv_dtype": call.kv_dtype,
+        "q_start": np.array([0, n0], dtype=np.int32), "kv_len": call.kv_len[:1],
+        "block_table": np.array([[remap[int(p)] for p in bt]], dtype=np.int32),
+        "q": bits(call.q[:n0]), "k": bits(call.k[:n0]), "v": bits(call.v[:n0]),
+        "gate": bits(call.gate[:n0]), "q_norm_w": bits(call.q_norm_w),
+        "k_norm_w": bits(call.k_norm_w), "gate_bias": bits(call.gate_bias),
+        "k_cache": bits(kc), "v_cache": bits(vc),
+        "k_scale": call.k_scale, "v_scale": call.v_scale,
+    }
+    rows = np.arange(n0 - rows_wanted, n0)
+    return inp, rows
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-rows", type=int, default=24, help="oracle rows per layer kind")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on exactly one GPU; --gpus {args.gpus} is not supported "
+              "(this build has no multi-GPU path)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import synth
+    from nope_gqa_attention_amd import beamattn as ba
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    ba.load()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    # ---------------------------------------------------------------- prefill workload
+    log("generating the long-prefill workload (8 x 2048 new on 98304 cached) ...")
+    staged = {}
+    for kind in ("full", "swa"):
+        call = synth.make_config(1, kind, cache_device="cuda")
+        staged[kind] = Staged(call)
+        log(f"  {kind}: {call.k_cache.shape[0]} pages staged")
+    q_lens = [int(x) for x in staged["full"].call.q_lens]
+    kv_lens = [int(x) for x in staged["full"].call.kv_len]
+    new_tokens = sum(q_lens)
+
+    parts = []
+    for kind in ("full", "swa"):
+        s = staged[kind]
+        parts.append((f"kvwrite_{kind}", s.kvwrite))
+        parts.append((f"prefill_{kind}", lambda s=s: s.attend("prefill")))
+    log(f"timing {args.steps} steps after {args.warmup} warmup ...")
+    ms_step, per = timed_steps(parts, args.steps, args.warmup)
+    flops = {k: 4 * D * HQ * visible_pairs(q_lens, kv_lens, k) for k in ("full", "swa")}
+    layers = {}
+    for k in ("full", "swa"):
+        t_attn = per[f"prefill_{k}"]
+        t_kv = per[f"kvwrite_{k}"]
+        tf = flops[k] / (t_attn * 1e-3) / 1e12
+        kv_bytes = new_tokens * (HQ * D * 2 * 2 + 2 * HKV * D * 2 * 2)   # q in/out, k/v in + cache
+        layers[k] = {
+            "ms": round(t_attn + t_kv, 4), "prefill_ms": round(t_attn, 4), "kvwrite_ms": round(t_kv, 4),
+            "tokens_per_s": round(new_tokens / ((t_attn + t_kv) * 1e-3), 1),
+            "prefill_tflops": round(tf, 2), "prefill_mfma_frac": round(tf / PEAK_BF16_TFLOPS, 4),
+            "algorithmic_tflop": round(flops[k] / 1e12, 4),
+            "kvwrite_gbs": round(kv_bytes / (t_kv * 1e-3) / 1e9, 1),
+        }
+    dom = layers["full"]
+    result = {
+        "metric": "attn tokens/s + %roofline (prefill MFMA TFLOP/s, decode HBM GB/s) per layer",
+        "value": round(new_tokens / (ms_step * 1e-3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "long prefill: 8 seqs x 2048 new tokens on 98304 cached, "
+                               "NoPE/SSMax full layer + SWA-512 layer, 48/8 heads, d128, "
+                               "64-token pages shuffled, bf16 KV",
+                   "global_batch": 8, "seq_len": 2048, "cached_tokens": 98304,
+                   "parallelism": "none (1 GPU)"},
+        "roofline": {"bound": "mfma", "achieved": dom["prefill_tflops"], "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": dom["prefill_mfma_frac"], "traffic": None,
+                     "kernel": "prefill_kernel (full NoPE layer)",
+                     "algorithmic_flop_per_launch": flops["full"]},
+        "layers": layers,
+    }
+    log(json.dumps(layers))
+    # free the prefill workload before the decode ones
+    cpu_inputs = []
+    if not args.no_cpu_baseline:
+        for kind in ("full", "swa"):
+            inp, rows = seq0_host_inputs(staged[kind].call, args.cpu_rows)
+            cpu_inputs.append((kind, inp, rows))
+    del staged, parts
+    torch.cuda.empty_cache()
+
+    # ---------------------------------------------------------------- decode workloads
+    if not args.no_decode:
+        dec = {}
+        for cfg in (2, 3, 4):
+            for kind in ("full", "swa"):
+                call = synth.make_config(cfg, kind, cache_device="cuda")
+                s = Staged(call)
+                ql = [int(x) for x in call.q_lens]
+                kl = [int(x) for x in call.kv_len]
+                copies = [s]
+                if cfg == 2 and kind == "full":
+                    # 409.6 MB of K/V would partly stay in the 256 MB MALL between
+                    # iterations: alternate between two copies at different addresses
+                    s2 = Staged(call)
+                    s2.cache = ba.DeviceCache(s.cache.k.clone(), s.cache.v.clone(),
+                                              call.k_scale, call.v_scale)
+                    copies.append(s2)
+                it = {"i": 0}
+
+                def run_attn(copies=copies, it=it):
+                    c = copies[it["i"] % len(copies)]
+                    it["i"] += 1
+                    c.attend("decode")
+                total, per_d = timed_steps([("kvwrite", s.kvwrite), ("decode", run_attn)],
+                                           max(args.steps, 5) * 2, args.warmup)
+                bpk = 2 * HKV * D * (2 if call.kv_dtype == "bf16" else 1)
+                nbytes = visible_keys_decode(ql, kl, kind) * bpk
+                gbs = nbytes / (per_d["decode"] * 1e-3) / 1e9
+                dec[f"config{cfg}-{kind}"] = {
+                    "kv_dtype": call.kv_dtype, "seqs": len(ql), "q_len": max(ql),
+                    "decode_us": round(per_d["decode"] * 1e3, 2),
+                    "kvwrite_us": round(per_d["kvwrite"] * 1e3, 2),
+                    "kv_bytes": nbytes, "hbm_gbs": round(gbs, 1),
+                    "hbm_frac": round(gbs / PEAK_HBM_GBS, 4),
+                    "tokens_per_s": round(sum(ql) / ((per_d["decode"] + per_d["kvwrite"]) * 1e-3), 1),
+                }
+                log(f"  decode config{cfg}-{kind}: {dec[f'config{cfg}-{kind}']}")
+                del s, copies, call
+                torch.cuda.empty_cache()
+        result["decode"] = dec
+
+    # ---------------------------------------------------------------- oracle on the host
+    if not args.no_cpu_baseline:
+        log("timing the fp64 oracle on the host ...")
+        rows, secs, cores = cpu_baseline(cpu_inputs, args.cpu_rows)
+        result["cpu_baseline"] = {
+            "value": round(rows / secs, 3), "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": f"last {args.cpu_rows} new tokens of sequence 0 in each layer kind "
+                      f"(full over 100,352 keys, SWA over 512), incl. that sequence's "
+                      f"kvwrite of 2048 tokens; {secs:.1f} s total",
+        }
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,332 @@
+// C ABI of libbeamattn: validates every host-visible argument, then launches the HIP
+// kernels on the caller's stream. No allocation, no synchronisation, no global mutable
+// state except the thread-local last-error message.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "beam_common.h"
+#include "beamattn.h"
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+beam_status fail(beam_status s, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+beam_status ok() {
+  g_last_error[0] = '\0';
+  return BEAM_OK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Decode work split: a workgroup (4 waves, one page per wave per step) covers
+// keys_per_split keys of one (sequence, KV head, row chunk). The split count aims at
+// about kDecodeTargetWorkgroups workgroups for a batch of max-length sequences, with
+// at least kDecodeMinKeysPerSplit keys each so the partial results stay small next to
+// the K/V bytes they summarise.
+constexpr int64_t kDecodeTargetWorkgroups = 1024;
+constexpr int64_t kDecodeMinKeysPerSplit = 1024;
+
+beam::DecodeSplit choose_decode_split(int32_t G, int32_t kind, int32_t window, int32_t num_seqs,
+                                      int32_t max_q_len, int64_t max_kv_len, int32_t Hkv) {
+  beam::DecodeSplit s{};
+  const int64_t rows = (int64_t)G * max_q_len;
+  s.row_chunks = (int32_t)((rows + beam::kDecodeMaxRowsPerChunk - 1) / beam::kDecodeMaxRowsPerChunk);
+  if (s.row_chunks < 1) s.row_chunks = 1;
+  s.rows_per_chunk = s.row_chunks == 1 ? (int32_t)(((rows + 15) / 16) * 16) : beam::kDecodeMaxRowsPerChunk;
+  if (s.rows_per_chunk < 16) s.rows_per_chunk = 16;
+  // keys a sequence visits, from its first visited page to its last key
+  int64_t range = max_kv_len;
+  if (kind == BEAM_LAYER_SWA) {
+    const int64_t w = (int64_t)window + max_q_len - 1 + (beam::kPage - 1);
+    if (w < range) range = w;
+  }
+  if (range < 1) range = 1;
+  const int64_t unit = (int64_t)num_seqs * Hkv * s.row_chunks;
+  int64_t want = unit > 0 ? (kDecodeTargetWorkgroups + unit - 1) / unit : 1;
+  if (want < 1) want = 1;
+  const int64_t step = beam::kDecodeKeysPerBlockStep;
+  int64_t kps = (range + want - 1) / want;
+  if (kps < kDecodeMinKeysPerSplit) kps = kDecodeMinKeysPerSplit;
+  kps = ((kps + step - 1) / step) * step;
+  s.keys_per_split = (int32_t)kps;
+  s.num_splits = (int32_t)((range + kps - 1) / kps);
+  if (s.num_splits < 1) s.num_splits = 1;
+  return s;
+}
+
+size_t decode_workspace_bytes(const beam::DecodeSplit& s, int32_t num_seqs, int32_t max_q_len,
+                              int32_t Hq) {
+  if (s.num_splits <= 1) return 0;
+  return (size_t)s.num_splits * (size_t)num_seqs * (size_t)max_q_len * (size_t)Hq *
+         (size_t)(beam::kHeadDim + 2) * sizeof(float);
+}
+
+beam_status check_layer(const beam_layer_desc* L, beam::LayerParams* out) {
+  if (!L) return fail(BEAM_ERR_INVALID_ARG, "layer descriptor is NULL");
+  if (L->head_dim != beam::kHeadDim)
+    return fail(BEAM_ERR_INVALID_ARG, "head_dim must be 128 (got %d)", L->head_dim);
+  if (L->page_size != beam::kPage)
+    return fail(BEAM_ERR_INVALID_ARG, "page_size must be 64 (got %d)", L->page_size);
+  if (L->num_q_heads <= 0 || L->num_kv_heads <= 0 || L->num_q_heads % L->num_kv_heads != 0)
+    return fail(BEAM_ERR_INVALID_ARG, "num_q_heads (%d) must be a positive multiple of num_kv_heads (%d)",
+                L->num_q_heads, L->num_kv_heads);
+  const int32_t G = L->num_q_heads / L->num_kv_heads;
+  if (G > 16) return fail(BEAM_ERR_INVALID_ARG, "at most 16 query heads per KV head (got %d)", G);
+  if (L->kind != BEAM_LAYER_SWA && L->kind != BEAM_LAYER_FULL)
+    return fail(BEAM_ERR_INVALID_ARG, "unknown layer kind %d", L->kind);
+  if (L->kind == BEAM_LAYER_SWA && L->window < 1)
+    return fail(BEAM_ERR_INVALID_ARG, "sliding window must be >= 1 (got %d)", L->window);
+  if (!(std::isfinite(L->sm_scale) && L->sm_scale > 0.f))
+    return fail(BEAM_ERR_INVALID_ARG, "sm_scale must be finite and > 0");
+  if (!(std::isfinite(L->rms_eps) && L->rms_eps >= 0.f))
+    return fail(BEAM_ERR_INVALID_ARG, "rms_eps must be finite and >= 0");
+  if (L->kind == BEAM_LAYER_SWA && !(std::isfinite(L->rope_theta) && L->rope_theta > 1.f))
+    return fail(BEAM_ERR_INVALID_ARG, "rope_theta must be finite and > 1");
+  if (L->kind == BEAM_LAYER_FULL &&
+      !(std::isfinite(L->ssmax_base) && L->ssmax_base > 0.f && std::isfinite(L->ssmax_exponent)))
+    return fail(BEAM_ERR_INVALID_ARG, "ssmax_base must be finite and > 0, ssmax_exponent finite");
+  *out = beam::LayerParams{L->num_q_heads, L->num_kv_heads, G, L->kind,
+                           L->kind == BEAM_LAYER_SWA ? L->window : 0, L->rope_theta, L->rms_eps,
+                           L->ssmax_base, L->ssmax_exponent, L->sm_scale};
+  return BEAM_OK;
+}
+
+beam_status check_batch(const beam_batch* B, beam::BatchParams* out) {
+  if (!B) return fail(BEAM_ERR_INVALID_ARG, "batch is NULL");
+  if (B->num_seqs < 0 || B->num_seqs > 65535)
+    return fail(BEAM_ERR_INVALID_ARG, "num_seqs must be in [0, 65535] (got %d)", B->num_seqs);
+  if (B->num_tokens < 0 || B->max_q_len < 0 || B->max_kv_len < 0 || B->max_pages < 0)
+    return fail(BEAM_ERR_INVALID_ARG, "negative batch bound");
+  if (B->num_tokens > (int64_t)B->num_seqs * B->max_q_len)
+    return fail(BEAM_ERR_INVALID_ARG, "num_tokens (%lld) exceeds num_seqs * max_q_len",
+                (long long)B->num_tokens);
+  if (B->num_tokens > 0x7FFFFFFF) return fail(BEAM_ERR_INVALID_ARG, "num_tokens too large");
+  if (B->max_q_len > B->max_kv_len)
+    return fail(BEAM_ERR_INVALID_ARG, "max_q_len exceeds max_kv_len");
+  if ((int64_t)B->max_pages * beam::kPage < B->max_kv_len)
+    return fail(BEAM_ERR_INVALID_ARG, "max_pages (%d) * 64 < max_kv_len (%lld)", B->max_pages,
+                (long long)B->max_kv_len);
+  if (B->num_seqs > 0 && (!B->q_start || !B->kv_len || !B->block_table))
+    return fail(BEAM_ERR_INVALID_ARG, "q_start, kv_len and block_table must be non-NULL");
+  *out = beam::BatchParams{B->num_seqs, B->q_start, B->kv_len, B->block_table,
+                           B->max_pages, B->max_q_len, B->max_kv_len, B->num_tokens};
+  return BEAM_OK;
+}
+
+beam_status check_cache(const beam_kv_cache* C, beam::CacheParams* out) {
+  if (!C) return fail(BEAM_ERR_INVALID_ARG, "cache is NULL");
+  if (!C->k || !C->v) return fail(BEAM_ERR_INVALID_ARG, "cache k/v pointers must be non-NULL");
+  if (!aligned16(C->k) || !aligned16(C->v))
+    return fail(BEAM_ERR_INVALID_ARG, "cache k/v must be 16-byte aligned");
+  if (C->num_pages <= 0) return fail(BEAM_ERR_INVALID_ARG, "cache num_pages must be > 0");
+  if (C->dtype != BEAM_KV_BF16 && C->dtype != BEAM_KV_FP8_E4M3)
+    return fail(BEAM_ERR_INVALID_ARG, "unknown cache dtype %d", C->dtype);
+  if (C->dtype == BEAM_KV_FP8_E4M3 &&
+      !(std::isfinite(C->k_scale) && C->k_scale > 0.f && std::isfinite(C->v_scale) && C->v_scale > 0.f))
+    return fail(BEAM_ERR_INVALID_ARG, "fp8 cache scales must be finite and > 0");
+  *out = beam::CacheParams{C->k, C->v, C->num_pages, C->dtype, C->k_scale, C->v_scale};
+  return BEAM_OK;
+}
+
+beam_status check_tensor(const char* name, const void* p, int64_t stride, int64_t min_stride,
+                         int64_t num_tokens) {
+  if (num_tokens == 0) return BEAM_OK;
+  if (!p) return fail(BEAM_ERR_INVALID_ARG, "%s is NULL", name);
+  if (!aligned16(p)) return fail(BEAM_ERR_INVALID_ARG, "%s must be 16-byte aligned", name);
+  if (stride < min_stride || stride % 8 != 0)
+    return fail(BEAM_ERR_INVALID_ARG, "%s token stride %lld must be >= %lld and a multiple of 8",
+                name, (long long)stride, (long long)min_stride);
+  return BEAM_OK;
+}
+
+beam_status check_gate(const void* gate, int64_t gate_stride, const void* bias, int32_t Hq,
+                       int64_t num_tokens) {
+  if (!gate) return BEAM_OK;
+  beam_status s = check_tensor("gate", gate, gate_stride, (int64_t)Hq * beam::kHeadDim, num_tokens);
+  if (s != BEAM_OK) return s;
+  if (!bias) return fail(BEAM_ERR_INVALID_ARG, "gate_bias is NULL while gate is given");
+  return BEAM_OK;
+}
+
+beam_status launched(hipError_t e) {
+  if (e != hipSuccess) return fail(BEAM_ERR_HIP, "HIP launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+bool ranges_overlap(const void* a, int64_t a_bytes, const void* b, int64_t b_bytes) {
+  const uintptr_t pa = reinterpret_cast<uintptr_t>(a), pb = reinterpret_cast<uintptr_t>(b);
+  return pa < pb + (uintptr_t)b_bytes && pb < pa + (uintptr_t)a_bytes;
+}
+
+}  // namespace
+
+extern "C" {
+
+beam_status beam_qknorm_rope_ssmax_kvwrite(const beam_layer_desc* layer, const beam_batch* batch,
+                                           const beam_kv_cache* cache, const void* q,
+                                           int64_t q_stride, const void* k, int64_t k_stride,
+                                           const void* v, int64_t v_stride, const void* q_norm_w,
+                                           const void* k_norm_w, int64_t norm_w_head_stride,
+                                           void* q_out, int64_t q_out_stride, void* stream) {
+  beam::LayerParams L;
+  beam::BatchParams B;
+  beam::CacheParams C;
+  beam_status s;
+  if ((s = check_layer(layer, &L)) != BEAM_OK) return s;
+  if ((s = check_batch(batch, &B)) != BEAM_OK) return s;
+  if ((s = check_cache(cache, &C)) != BEAM_OK) return s;
+  const int64_t N = B.num_tokens;
+  if ((s = check_tensor("q", q, q_stride, (int64_t)L.Hq * beam::kHeadDim, N)) != BEAM_OK) return s;
+  if ((s = check_tensor("k", k, k_stride, (int64_t)L.Hkv * beam::kHeadDim, N)) != BEAM_OK) return s;
+  if ((s = check_tensor("v", v, v_stride, (int64_t)L.Hkv * beam::kHeadDim, N)) != BEAM_OK) return s;
+  if ((s = check_tensor("q_out", q_out, q_out_stride, (int64_t)L.Hq * beam::kHeadDim, N)) != BEAM_OK) return s;
+  if (N > 0) {
+    if (!q_norm_w || !k_norm_w || !aligned16(q_norm_w) || !aligned16(k_norm_w))
+      return fail(BEAM_ERR_INVALID_ARG, "norm weights must be non-NULL and 16-byte aligned");
+    if (norm_w_head_stride != 0 && (norm_w_head_stride < beam::kHeadDim || norm_w_head_stride % 8 != 0))
+      return fail(BEAM_ERR_INVALID_ARG, "norm_w_head_stride must be 0 or >= 128 and a multiple of 8");
+    if (q_out != q) {
+      const int64_t qb = ((N - 1) * q_stride + (int64_t)L.Hq * beam::kHeadDim) * 2;
+      const int64_t ob = ((N - 1) * q_out_stride + (int64_t)L.Hq * beam::kHeadDim) * 2;
+      if (ranges_overlap(q, qb, q_out, ob))
+        return fail(BEAM_ERR_INVALID_ARG, "q_out overlaps q without being the same buffer");
+    } else if (q_out_stride != q_stride) {
+      return fail(BEAM_ERR_INVALID_ARG, "in-place q_out needs q_out_stride == q_stride");
+    }
+  }
+  return launched(beam::launch_qknorm_kvwrite(L, B, C, q, q_stride, k, k_stride, v, v_stride,
+                                              q_norm_w, k_norm_w, norm_w_head_stride, q_out,
+                                              q_out_stride, static_cast<hipStream_t>(stream)));
+}
+
+beam_status beam_attn_prefill(const beam_layer_desc* layer, const beam_batch* batch,
+                              const beam_kv_cache* cache, const void* q, int64_t q_stride,
+                              const void* gate, int64_t gate_stride, const void* gate_bias,
+                              void* out, int64_t out_stride, void* stream) {
+  beam::LayerParams L;
+  beam::BatchParams B;
+  beam::CacheParams C;
+  beam_status s;
+  if ((s = check_layer(layer, &L)) != BEAM_OK) return s;
+  if ((s = check_batch(batch, &B)) != BEAM_OK) return s;
+  if ((s = check_cache(cache, &C)) != BEAM_OK) return s;
+  if (C.dtype != BEAM_KV_BF16)
+    return fail(BEAM_ERR_UNSUPPORTED, "prefill over an fp8 cache is not implemented");
+  const int64_t N = B.num_tokens;
+  const int64_t row = (int64_t)L.Hq * beam::kHeadDim;
+  if ((s = check_tensor("q", q, q_stride, row, N)) != BEAM_OK) return s;
+  if ((s = check_tensor("out", out, out_stride, row, N)) != BEAM_OK) return s;
+  if ((s = check_gate(gate, gate_stride, gate_bias, L.Hq, N)) != BEAM_OK) return s;
+  const int64_t tiles = ((int64_t)B.max_q_len * L.G + 255) / 256;
+  if (tiles > 0x7FFFFFFF) return fail(BEAM_ERR_INVALID_ARG, "max_q_len too large");
+  return launched(beam::launch_attn_prefill(L, B, C, q, q_stride, gate, gate_stride, gate_bias,
+                                            out, out_stride, static_cast<hipStream_t>(stream)));
+}
+
+size_t beam_attn_decode_workspace_bytes(const beam_layer_desc* layer, int32_t num_seqs,
+                                        int32_t max_q_len, int64_t max_kv_len) {
+  beam::LayerParams L;
+  if (check_layer(layer, &L) != BEAM_OK) return 0;
+  if (num_seqs < 0 || max_q_len < 1 || max_q_len > 16 || max_kv_len < max_q_len) return 0;
+  const beam::DecodeSplit s =
+      choose_decode_split(L.G, L.kind, L.window, num_seqs, max_q_len, max_kv_len, L.Hkv);
+  return decode_workspace_bytes(s, num_seqs, max_q_len, L.Hq);
+}
+
+beam_status beam_attn_decode(const beam_layer_desc* layer, const beam_batch* batch,
+                             const beam_kv_cache* cache, const void* q, int64_t q_stride,
+                             const void* gate, int64_t gate_stride, const void* gate_bias,
+                             void* out, int64_t out_stride, void* workspace,
+                             size_t workspace_bytes, void* stream) {
+  beam::LayerParams L;
+  beam::BatchParams B;
+  beam::CacheParams C;
+  beam_status s;
+  if ((s = check_layer(layer, &L)) != BEAM_OK) return s;
+  if ((s = check_batch(batch, &B)) != BEAM_OK) return s;
+  if ((s = check_cache(cache, &C)) != BEAM_OK) return s;
+  if (B.max_q_len < 1 || B.max_q_len > 16)
+    return fail(BEAM_ERR_INVALID_ARG, "decode needs max_q_len in 1..16 (got %d)", B.max_q_len);
+  const int64_t N = B.num_tokens;
+  const int64_t row = (int64_t)L.Hq * beam::kHeadDim;
+  if ((s = check_tensor("q", q, q_stride, row, N)) != BEAM_OK) return s;
+  if ((s = check_tensor("out", out, out_stride, row, N)) != BEAM_OK) return s;
+  if ((s = check_gate(gate, gate_stride, gate_bias, L.Hq, N)) != BEAM_OK) return s;
+  const beam::DecodeSplit S = choose_decode_split(L.G, L.kind, L.window, B.num_seqs, B.max_q_len,
+                                                  B.max_kv_len, L.Hkv);
+  const size_t need = decode_workspace_bytes(S, B.num_seqs, B.max_q_len, L.Hq);
+  if (need > 0) {
+    if (!workspace || workspace_bytes < need)
+      return fail(BEAM_ERR_WORKSPACE, "decode workspace needs %zu bytes (got %zu%s)", need,
+                  workspace_bytes, workspace ? "" : ", NULL pointer");
+    if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+      return fail(BEAM_ERR_INVALID_ARG, "decode workspace must be 256-byte aligned");
+  }
+  return launched(beam::launch_attn_decode(L, B, C, S, q, q_stride, gate, gate_stride, gate_bias,
+                                           out, out_stride, workspace,
+                                           static_cast<hipStream_t>(stream)));
+}
+
+beam_status beam_head_gate(const beam_layer_desc* layer, int64_t num_tokens, const void* attn,
+                           int64_t attn_stride, const void* gate, int64_t gate_stride,
+                           const void* gate_bias, void* out, int64_t out_stride, void* stream) {
+  beam::LayerParams L;
+  beam_status s;
+  if ((s = check_layer(layer, &L)) != BEAM_OK) return s;
+  if (num_tokens < 0) return fail(BEAM_ERR_INVALID_ARG, "num_tokens must be >= 0");
+  const int64_t row = (int64_t)L.Hq * beam::kHeadDim;
+  if ((s = check_tensor("attn", attn, attn_stride, row, num_tokens)) != BEAM_OK) return s;
+  if ((s = check_tensor("out", out, out_stride, row, num_tokens)) != BEAM_OK) return s;
+  if (num_tokens > 0 && !gate) return fail(BEAM_ERR_INVALID_ARG, "gate is NULL");
+  if ((s = check_gate(gate, gate_stride, gate_bias, L.Hq, num_tokens)) != BEAM_OK) return s;
+  if (out != attn && num_tokens > 0) {
+    const int64_t ab = ((num_tokens - 1) * attn_stride + row) * 2;
+    const int64_t ob = ((num_tokens - 1) * out_stride + row) * 2;
+    if (ranges_overlap(attn, ab, out, ob))
+      return fail(BEAM_ERR_INVALID_ARG, "out overlaps attn without being the same buffer");
+  } else if (out == attn && attn_stride != out_stride) {
+    return fail(BEAM_ERR_INVALID_ARG, "in-place gate needs out_stride == attn_stride");
+  }
+  return launched(beam::launch_head_gate(L, num_tokens, attn, attn_stride, gate, gate_stride,
+                                         gate_bias, out, out_stride,
+                                         static_cast<hipStream_t>(stream)));
+}
+
+uint64_t beam_kv_bytes_per_token(int32_t num_full_layers, int32_t num_kv_heads, int32_t head_dim,
+                                 int32_t dtype) {
+  if (num_full_layers < 0 || num_kv_heads < 0 || head_dim < 0) return 0;
+  uint64_t bytes;
+  if (dtype == BEAM_KV_BF16) bytes = 2;
+  else if (dtype == BEAM_KV_FP8_E4M3) bytes = 1;
+  else return 0;
+  return (uint64_t)num_full_layers * 2u * (uint64_t)num_kv_heads * (uint64_t)head_dim * bytes;
+}
+
+const char* beam_status_string(beam_status status) {
+  switch (status) {
+    case BEAM_OK: return "ok";
+    case BEAM_ERR_INVALID_ARG: return "invalid argument";
+    case BEAM_ERR_UNSUPPORTED: return "unsupported";
+    case BEAM_ERR_WORKSPACE: return "workspace too small";
+    case BEAM_ERR_HIP: return "HIP error";
+  }
+  return "unknown status";
+}
+
+const char* beam_last_error(void) { return g_last_error; }
+
+int32_t beam_abi_version(void) { return BEAM_ABI_VERSION; }
+
+}  // extern "C"

@@ -1,0 +1,132 @@
+// Internal header of libbeamattn: launch parameter blocks passed from the validating C
+// ABI layer (api.cpp) to the kernel launchers, plus small device helpers shared by the
+// kernels. Everything here targets gfx950 (CDNA4, wave64) only.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "beamattn.h"
+
+namespace beam {
+
+constexpr int kHeadDim = 128;
+constexpr int kPage = 64;
+
+// ---------------------------------------------------------------- launch parameters
+
+struct LayerParams {
+  int32_t Hq, Hkv, G;          // query heads, KV heads, query heads per KV head
+  int32_t kind;                // beam_layer_kind
+  int32_t window;              // sliding-window length in keys (own key included)
+  float rope_theta, rms_eps, ssmax_base, ssmax_exponent, sm_scale;
+};
+
+struct BatchParams {
+  int32_t num_seqs;
+  const int32_t* q_start;
+  const int32_t* kv_len;
+  const int32_t* block_table;
+  int32_t max_pages;
+  int32_t max_q_len;
+  int64_t max_kv_len;
+  int64_t num_tokens;
+};
+
+struct CacheParams {
+  void* k;
+  void* v;
+  int64_t num_pages;
+  int32_t dtype;               // beam_kv_dtype
+  float k_scale, v_scale;
+};
+
+// Decode split geometry, chosen on the host from the batch bounds (the same function
+// sizes the workspace).
+struct DecodeSplit {
+  int32_t num_splits;          // splits per (sequence, KV head, row chunk)
+  int32_t keys_per_split;      // multiple of kDecodeKeysPerBlockStep
+  int32_t row_chunks;          // ceil(G * max_q_len / kDecodeRowsPerChunk)
+  int32_t rows_per_chunk;      // 16, 32 or 48 (a multiple of 16)
+};
+
+constexpr int kDecodeWaves = 4;                       // waves per decode workgroup
+constexpr int kDecodeKeysPerBlockStep = kDecodeWaves * kPage;  // one page per wave per step
+constexpr int kDecodeMaxRowsPerChunk = 48;
+
+hipError_t launch_qknorm_kvwrite(const LayerParams& L, const BatchParams& B, const CacheParams& C,
+                                 const void* q, int64_t q_stride, const void* k, int64_t k_stride,
+                                 const void* v, int64_t v_stride, const void* q_norm_w,
+                                 const void* k_norm_w, int64_t norm_w_head_stride, void* q_out,
+                                 int64_t q_out_stride, hipStream_t stream);
+
+hipError_t launch_head_gate(const LayerParams& L, int64_t num_tokens, const void* attn,
+                            int64_t attn_stride, const void* gate, int64_t gate_stride,
+                            const void* gate_bias, void* out, int64_t out_stride,
+                            hipStream_t stream);
+
+hipError_t launch_attn_decode(const LayerParams& L, const BatchParams& B, const CacheParams& C,
+                              const DecodeSplit& S, const void* q, int64_t q_stride,
+                              const void* gate, int64_t gate_stride, const void* gate_bias,
+                              void* out, int64_t out_stride, void* workspace, hipStream_t stream);
+
+hipError_t launch_attn_prefill(const LayerParams& L, const BatchParams& B, const CacheParams& C,
+                               const void* q, int64_t q_stride, const void* gate,
+                               int64_t gate_stride, const void* gate_bias, void* out,
+                               int64_t out_stride, hipStream_t stream);
+
+// ---------------------------------------------------------------- device helpers
+
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8_t;
+typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2_t;
+typedef __attribute__((__vector_size__(4 * sizeof(short)))) short i16x4_t;
+typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16_t;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4_t;
+typedef __attribute__((__vector_size__(4 * sizeof(uint32_t)))) uint32_t u32x4_t;
+typedef __attribute__((__vector_size__(2 * sizeof(uint32_t)))) uint32_t u32x2_t;
+
+__device__ __forceinline__ float bf16_to_f32(uint32_t bits16) {
+  return __uint_as_float(bits16 << 16);
+}
+
+// Two floats -> two bf16 (round to nearest even, NaN stays NaN), packed low/high.
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  bf16x2_t r;
+  r[0] = (__bf16)lo;
+  r[1] = (__bf16)hi;
+  return __builtin_bit_cast(uint32_t, r);
+}
+
+__device__ __forceinline__ uint32_t bf16_bits_rne(float f) {
+  return pack_bf16x2(f, 0.0f) & 0xFFFFu;
+}
+
+// OCP E4M3FN encode with saturation: |x| >= 448 -> +-448, NaN -> 0x7F, otherwise the
+// nearest representable value with ties to even mantissa. Written from the format: 4
+// exponent bits with bias 7 (normals 2^-6 .. 2^8), 3 mantissa bits, subnormals M * 2^-9.
+__device__ __forceinline__ uint32_t f32_to_e4m3_sat(float x) {
+  const uint32_t u = __float_as_uint(x);
+  const uint32_t sign = (u >> 24) & 0x80u;
+  const uint32_t a = u & 0x7FFFFFFFu;
+  if (a > 0x7F800000u) return 0x7Fu;                  // NaN
+  if (a >= 0x43E00000u) return sign | 0x7Eu;          // >= 448 (incl. inf) saturates
+  const int e = (int)(a >> 23) - 127;
+  if (e >= -6) {                                       // normal range of e4m3
+    uint32_t q = (a >> 20) & 7u;                       // top 3 mantissa bits
+    const uint32_t rem = a & 0xFFFFFu;
+    const uint32_t up = (rem > 0x80000u) || (rem == 0x80000u && (q & 1u));
+    uint32_t code = ((uint32_t)(e + 7) << 3) + q + up;   // carry into exponent is exact
+    return sign | code;
+  }
+  // subnormal: value / 2^-9 rounded to an integer (ties to even); 8 becomes 2^-6 (0x08)
+  const float t = __uint_as_float(a) * 512.0f;         // exact power-of-two scaling
+  const uint32_t m = (uint32_t)__builtin_rintf(t);
+  return sign | m;
+}
+
+// Wave-wide helpers (wave64).
+__device__ __forceinline__ float wave_xor_max(float v, int mask) {
+  return fmaxf(v, __shfl_xor(v, mask, 64));
+}
+
+}  // namespace beam

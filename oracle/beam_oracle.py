@@ -32,7 +32,8 @@ Readings taken where the pages are silent (each is listed in the design notes):
   * Query head h reads KV head floor(h / (Hq/Hkv)).
   * gate column h*128 + d; per-head bias broadcast over d; V is not normalised.
   * New tokens in one call see earlier new tokens and themselves (causal block).
-  * fp8 is OCP E4M3FN with saturating round-to-nearest-even; stored = e4m3(k'/scale).
+  * fp8 is OCP E4M3FN with saturating round-to-nearest-even; stored = e4m3(k'/scale),
+    the quotient formed as one binary32 division (the precision that decides the code).
 
 Parity status: every function below is pinned by the CPU test-suite against closed
 forms, library routines or invariants, except the readings above that no page fixes
@@ -249,13 +250,20 @@ def store_kv(cache, block_table, seq, pos, values_bits, kv_dtype: str, scale: fl
     """Write new K (or V) rows into a copy of `cache` at their physical slots.
     values_bits: [N, Hkv, D] bf16 bits (k' after norm/rotation, or raw v).
     bf16 cache stores the bits unchanged; fp8 cache stores e4m3(value / scale).
+
+    The fp8 code is an integer decided by floating point: value / scale is formed as
+    one IEEE binary32 division (the kernel's precision; the pages fix none) and that
+    quotient is rounded to e4m3. Forming it in fp64 instead moves about 1% of codes by
+    one step: the scale amax/448 is itself an fp32 rounding, so quotients fall within
+    2^-24 of an e4m3 midpoint far more often than chance.
     """
     out = np.array(cache, copy=True)
     page, slot = physical_slot(block_table, seq, pos)
     if kv_dtype == "bf16":
         out[page, :, slot, :] = np.asarray(values_bits, dtype=np.uint16)
     elif kv_dtype == "fp8":
-        out[page, :, slot, :] = f64_to_e4m3(bf16_bits_to_f64(values_bits) / float(scale))
+        quotient = bf16_bits_to_f64(values_bits).astype(np.float32) / np.float32(scale)
+        out[page, :, slot, :] = f64_to_e4m3(quotient.astype(np.float64))
     else:
         raise ValueError(kv_dtype)
     return out
@@ -332,32 +340,48 @@ def attention_rows(q_bits, k_cache, v_cache, block_table, seq, pos, kind: str,
 def attention_rows_long(q_bits, k_cache, v_cache, block_table, seq, pos, kind: str,
                         kv_dtype: str, k_scale: float = 1.0, v_scale: float = 1.0,
                         sm_scale: float = SM_SCALE, window: int = WINDOW,
-                        key_chunk: int = 1 << 18):
-    """Same result as attention_rows, for rows over very long contexts: the visible
-    keys are read one KV head and one chunk at a time, the scores kept in full, and
-    the softmax done in two passes exactly as defined (max, then exp/sum/weights)."""
+                        key_chunk: int = 1 << 16):
+    """Same result as attention_rows, for rows over very long contexts.
+
+    Rows of one sequence are taken together; their keys are read one chunk at a time
+    and each row's softmax is done in the textbook two passes: first the maximum of its
+    visible scores, then exp(z - max), their sum and the weighted sum of V. Keys outside
+    a row's visible range get weight exactly 0.
+    """
     q_hat = bf16_bits_to_f64(q_bits)
     R, Hq, D = q_hat.shape
     Hkv = np.asarray(k_cache).shape[1]
     G = Hq // Hkv
     o = np.empty((R, Hq, D), dtype=np.float64)
-    for r in range(R):
-        lo, hi = visible_range(int(pos[r]), kind, window)
-        b = int(seq[r])
-        for g in range(Hkv):
-            qg = q_hat[r, g * G:(g + 1) * G, :]                  # [G, D]
-            z = np.empty((G, hi - lo + 1), dtype=np.float64)
-            for s in range(lo, hi + 1, key_chunk):
-                keys = np.arange(s, min(hi + 1, s + key_chunk))
-                kk = read_kv(k_cache, block_table, b, keys, kv_dtype, k_scale)[:, g, :]
-                z[:, s - lo:s - lo + len(keys)] = sm_scale * (qg @ kk.T)
-            p = softmax(z, axis=-1)
-            acc = np.zeros((G, D), dtype=np.float64)
-            for s in range(lo, hi + 1, key_chunk):
-                keys = np.arange(s, min(hi + 1, s + key_chunk))
-                vv = read_kv(v_cache, block_table, b, keys, kv_dtype, v_scale)[:, g, :]
-                acc += p[:, s - lo:s - lo + len(keys)] @ vv
-            o[r, g * G:(g + 1) * G, :] = acc
+    seq = np.asarray(seq, dtype=np.int64)
+    pos = np.asarray(pos, dtype=np.int64)
+    for b in np.unique(seq):
+        rows = np.nonzero(seq == b)[0]
+        lo_r = np.array([visible_range(int(pos[r]), kind, window)[0] for r in rows])
+        hi_r = pos[rows]
+        qb = q_hat[rows].reshape(len(rows), Hkv, G, D)                  # [r, g, G, D]
+        m = np.full((len(rows), Hkv, G), -np.inf)
+        chunks = range(int(lo_r.min()), int(hi_r.max()) + 1, key_chunk)
+
+        def scores(s0):
+            keys = np.arange(s0, min(int(hi_r.max()) + 1, s0 + key_chunk))
+            kk = read_kv(k_cache, block_table, int(b), keys, kv_dtype, k_scale)   # [n, g, D]
+            z = sm_scale * np.matmul(qb, kk.transpose(1, 2, 0)[None])          # [r, g, G, n]
+            vis = (keys[None, :] >= lo_r[:, None]) & (keys[None, :] <= hi_r[:, None])
+            return keys, np.where(vis[:, None, None, :], z, -np.inf)
+
+        for s0 in chunks:                                   # pass 1: row maxima
+            _, z = scores(s0)
+            m = np.maximum(m, z.max(axis=-1))
+        ssum = np.zeros_like(m)
+        acc = np.zeros((len(rows), Hkv, G, D))
+        for s0 in chunks:                                   # pass 2: weights, sums, PV
+            keys, z = scores(s0)
+            e = np.exp(z - m[..., None])
+            ssum += e.sum(axis=-1)
+            vv = read_kv(v_cache, block_table, int(b), keys, kv_dtype, v_scale)
+            acc += np.matmul(e, vv.transpose(1, 0, 2)[None])                    # [r, g, G, D]
+        o[rows] = (acc / ssum[..., None]).reshape(len(rows), Hq, D)
     return o
 
 

@@ -116,11 +116,15 @@ class LayerCall:
 
 
 def make_call(q_lens, kv_lens, kind: str, kv_dtype: str, seed, name: str = "case",
-              spare_pages: int = 3, window: int = WINDOW) -> LayerCall:
+              spare_pages: int = 3, window: int = WINDOW, cache_device=None) -> LayerCall:
     """A layer call with the given new-token counts and total key counts per sequence.
 
     Draw order: page permutation, q, k, v, gate, q_norm_w, k_norm_w, gate_bias,
-    cached K, cached V (each from its own seeded stream).
+    cached K, cached V (each from its own seeded stream). With cache_device set (e.g.
+    "cuda"), the cached K/V are drawn on that device by torch's seeded Philox generator
+    instead of numpy (same distributions, different values, much faster for the
+    multi-GiB caches); everything else is unchanged. The returned caches then live on
+    that device.
     """
     q_lens = np.asarray(q_lens, dtype=np.int64)
     kv_lens = np.asarray(kv_lens, dtype=np.int64)
@@ -163,8 +167,12 @@ def make_call(q_lens, kv_lens, kind: str, kv_dtype: str, seed, name: str = "case
     # that hold no cached token yet (new tokens' slots, tails, the shared NaN page).
     shape = (num_pages, HKV, PAGE, D)
     n_cache = num_pages * HKV * PAGE * D
-    kc = _normal_bf16(n_cache, key + [9]).view(shape)
-    vc = _normal_bf16(n_cache, key + [10]).view(shape)
+    if cache_device is None:
+        kc = _normal_bf16(n_cache, key + [9]).view(shape)
+        vc = _normal_bf16(n_cache, key + [10]).view(shape)
+    else:
+        kc = _normal_bf16_device(n_cache, key + [9], cache_device).view(shape)
+        vc = _normal_bf16_device(n_cache, key + [10], cache_device).view(shape)
     un_p, un_s = [], []
     for b in range(B):
         cached = int(kv_lens[b] - q_lens[b])
@@ -176,11 +184,11 @@ def make_call(q_lens, kv_lens, kind: str, kv_dtype: str, seed, name: str = "case
     if has_poison:
         un_p.extend([poison] * PAGE)
         un_s.extend(range(PAGE))
-    un_p = torch.tensor(un_p, dtype=torch.long)
-    un_s = torch.tensor(un_s, dtype=torch.long)
+    un_p = torch.tensor(un_p, dtype=torch.long, device=kc.device)
+    un_s = torch.tensor(un_s, dtype=torch.long, device=kc.device)
     k_scale = v_scale = 1.0
     if kv_dtype == "bf16":
-        nan = torch.tensor(BF16_NAN, dtype=torch.int16).view(torch.bfloat16)
+        nan = torch.tensor(BF16_NAN, dtype=torch.int16).view(torch.bfloat16).to(kc.device)
         kc[un_p, :, un_s, :] = nan
         vc[un_p, :, un_s, :] = nan
     elif kv_dtype == "fp8":
@@ -218,6 +226,22 @@ def _normal_bf16(n: int, key) -> torch.Tensor:
     return out
 
 
+def _normal_bf16_device(n: int, key, device) -> torch.Tensor:
+    """n standard normals rounded to bf16, drawn on `device` by torch's Philox generator
+    seeded from `key`, chunk by chunk."""
+    out = torch.empty(n, dtype=torch.bfloat16, device=device)
+    gen = torch.Generator(device=device)
+    seed = 0
+    for k in key:
+        seed = (seed * 1000003 + int(k) + 1) % (1 << 62)
+    gen.manual_seed(seed)
+    step = 1 << 26
+    for s in range(0, n, step):
+        e = min(n, s + step)
+        out[s:e] = torch.randn(e - s, generator=gen, device=device, dtype=torch.float32).to(torch.bfloat16)
+    return out
+
+
 def _amax(x: torch.Tensor) -> float:
     flat = x.reshape(-1)
     step = 1 << 26
@@ -229,7 +253,7 @@ def _amax(x: torch.Tensor) -> float:
 
 def _fp8_codes(x_bf16: torch.Tensor, scale: float) -> torch.Tensor:
     """fp8 e4m3 codes of cached values x/scale (torch's cast after an explicit clamp)."""
-    out = torch.empty(x_bf16.shape, dtype=torch.uint8)
+    out = torch.empty(x_bf16.shape, dtype=torch.uint8, device=x_bf16.device)
     flat_x = x_bf16.reshape(-1)
     flat_o = out.view(-1)
     step = 1 << 26
@@ -259,11 +283,11 @@ def config_shapes(cfg: int):
     raise ValueError(cfg)
 
 
-def make_config(cfg: int, kind: str, seed: int | None = None) -> LayerCall:
+def make_config(cfg: int, kind: str, seed: int | None = None, cache_device=None) -> LayerCall:
     """Workload `cfg` (0..4) for one layer kind ("swa" or "full"); seed defaults to cfg."""
     q_lens, kv_lens, kv_dtype, desc = config_shapes(cfg)
     seed = cfg if seed is None else seed
     call = make_call(q_lens, kv_lens, kind, kv_dtype, [seed, 0 if kind == "swa" else 1],
-                     name=f"config{cfg}-{kind}")
+                     name=f"config{cfg}-{kind}", cache_device=cache_device)
     call.extra["description"] = desc
     return call

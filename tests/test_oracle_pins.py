@@ -341,6 +341,20 @@ def test_fp8_store_roundtrip_error_bound():
     assert np.all(err <= np.maximum(np.abs(x) * 2 ** -4, 2 ** -10 * inp["v_scale"]) * (1 + 1e-12))
 
 
+def test_fp8_store_matches_torch_fp32_division_and_cast():
+    """The stored code is e4m3 of the binary32 quotient value/scale: torch's fp32
+    division and (clamped) e4m3 cast give the same codes."""
+    c = synth.make_call([200], [260], "full", "fp8", [18, 1])
+    inp = c.oracle_inputs()
+    seq, pos = O.new_token_positions(inp["q_start"], inp["kv_len"])
+    vc = O.store_kv(inp["v_cache"], inp["block_table"], seq, pos, inp["v"], "fp8", inp["v_scale"])
+    page, slot = O.physical_slot(inp["block_table"], seq, pos)
+    ours = vc[page, :, slot, :]
+    quot = c.v.float() / torch.tensor(inp["v_scale"], dtype=torch.float32)
+    ref = quot.clamp(-448, 448).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(ours, ref)
+
+
 def test_block_is_causal_within_itself():
     c = synth.make_call([6], [200], "full", "bf16", [13, 1])
     inp = c.oracle_inputs()
@@ -465,4 +479,13 @@ def test_long_context_path_equals_short_path():
                          "full", "fp8", inp["k_scale"], inp["v_scale"])
     b = O.attention_rows_long(q, inp["k_cache"], inp["v_cache"], inp["block_table"], seq, pos - 5,
                               "full", "fp8", inp["k_scale"], inp["v_scale"], key_chunk=333)
+    c2 = synth.make_call([3, 1], [900, 700], "swa", "bf16", [17, 0])
+    inp = c2.oracle_inputs()
+    seq, pos = O.new_token_positions(inp["q_start"], inp["kv_len"])
+    q = O.prepare_qk(inp["q"], inp["q_norm_w"], pos, "swa", True)
+    kc = O.store_kv(inp["k_cache"], inp["block_table"], seq, pos, inp["k"], "bf16")
+    vc = O.store_kv(inp["v_cache"], inp["block_table"], seq, pos, inp["v"], "bf16")
+    a2 = O.attention_rows(q, kc, vc, inp["block_table"], seq, pos, "swa", "bf16")
+    b2 = O.attention_rows_long(q, kc, vc, inp["block_table"], seq, pos, "swa", "bf16", key_chunk=100)
+    np.testing.assert_allclose(a2, b2, atol=1e-13, rtol=0)
     np.testing.assert_allclose(a, b, atol=1e-13, rtol=0)
