@@ -32,11 +32,10 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 
 // Decode work split: a workgroup (4 waves, one page per wave per step) covers
 // keys_per_split keys of one (sequence, KV head, row chunk). The split count aims at
-// about kDecodeTargetWorkgroups workgroups for a batch of max-length sequences, with
-// at least kDecodeMinKeysPerSplit keys each so the partial results stay small next to
-// the K/V bytes they summarise.
-constexpr int64_t kDecodeTargetWorkgroups = 1024;
-constexpr int64_t kDecodeMinKeysPerSplit = 1024;
+// about kDecodeTargetWorkgroups workgroups for a batch of max-length sequences. A split
+// is at least as long as keeps its partial results (rows x 130 fp32 written, then read
+// by the merge) near 1.5% of the fp8 K/V bytes it reads (256 bytes per key).
+constexpr int64_t kDecodeTargetWorkgroups = 2048;
 
 beam::DecodeSplit choose_decode_split(int32_t G, int32_t kind, int32_t window, int32_t num_seqs,
                                       int32_t max_q_len, int64_t max_kv_len, int32_t Hkv) {
@@ -57,8 +56,10 @@ beam::DecodeSplit choose_decode_split(int32_t G, int32_t kind, int32_t window, i
   int64_t want = unit > 0 ? (kDecodeTargetWorkgroups + unit - 1) / unit : 1;
   if (want < 1) want = 1;
   const int64_t step = beam::kDecodeKeysPerBlockStep;
+  const int64_t rows_in_chunk = rows < s.rows_per_chunk ? rows : s.rows_per_chunk;
+  const int64_t min_keys = rows_in_chunk * (beam::kHeadDim + 2) * 4 * 64 / 256;
   int64_t kps = (range + want - 1) / want;
-  if (kps < kDecodeMinKeysPerSplit) kps = kDecodeMinKeysPerSplit;
+  if (kps < min_keys) kps = min_keys;
   kps = ((kps + step - 1) / step) * step;
   s.keys_per_split = (int32_t)kps;
   s.num_splits = (int32_t)((range + kps - 1) / kps);

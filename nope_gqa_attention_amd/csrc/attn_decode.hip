@@ -72,7 +72,7 @@ __device__ __forceinline__ int64_t range_base(const LayerParams& L, int64_t kv, 
 }
 
 template <int KV, int RB>
-__global__ __launch_bounds__(kThreads) void decode_split_kernel(
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(RB == 1 ? 2 : 1))) void decode_split_kernel(
     LayerParams L, BatchParams B, CacheParams C, DecodeSplit S,
     const uint16_t* __restrict__ q, int64_t q_stride, const uint16_t* __restrict__ gate,
     int64_t gate_stride, const uint16_t* __restrict__ gate_bias, uint16_t* out,
@@ -142,128 +142,181 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(
   unsigned char* vlds = lds + wave * kVRowsPerWave * kVRowBytes;
   const int64_t head_elems = (int64_t)kPage * kHeadDim;   // one KV head's page
 
-  for (int64_t pk = k_begin + (int64_t)wave * kPage; pk < k_end; pk += kDecodeWaves * kPage) {
-    const int64_t page = B.block_table[(int64_t)b * B.max_pages + pk / kPage];
+  // This wave's pages: keys pk = k_begin + 64*(wave + 4*pi), pi = 0, 1, ...; each page is
+  // two half-steps of 32 keys. Half-step j+1 is fetched into registers while half-step j
+  // is computed, so every wave keeps one half-page of K and V in flight.
+  const int64_t first_pk = k_begin + (int64_t)kPage * wave;
+  int n_half = 0;
+  if (first_pk < k_end) {
+    const int64_t n_pages = (k_end - first_pk + kDecodeKeysPerBlockStep - 1) / kDecodeKeysPerBlockStep;
+    const int64_t last_pk = first_pk + (n_pages - 1) * kDecodeKeysPerBlockStep;
+    n_half = (int)(2 * (n_pages - 1) + (last_pk + 32 < k_end ? 2 : 1));
+  }
+  // block-table entries of the wave's pages, 64 at a time: lane i holds page i of the chunk
+  const int32_t* bt_row = B.block_table + (int64_t)b * B.max_pages;
+  int bt_chunk = -1;
+  int32_t bt_lane = 0;
+  auto page_of = [&](int pi) -> int64_t {
+    if (pi / 64 != bt_chunk) {
+      bt_chunk = pi / 64;
+      const int64_t my_pk = first_pk + (int64_t)kDecodeKeysPerBlockStep * (64 * bt_chunk + lane);
+      bt_lane = my_pk < k_end ? bt_row[my_pk / kPage] : 0;
+    }
+    return (int64_t)__builtin_amdgcn_readlane(bt_lane, pi % 64);
+  };
+
+  constexpr int kKRegs = KV == BEAM_KV_BF16 ? 8 : 4;   // 16-byte K loads per lane per half-step
+  constexpr int kVRegs = KV == BEAM_KV_BF16 ? 8 : 4;   // 16-byte V loads per lane per half-step
+  u32x4_t kreg[kKRegs], vreg[kVRegs], kreg_n[kKRegs], vreg_n[kVRegs];
+
+  auto fetch = [&](int j, u32x4_t* kr, u32x4_t* vr) {
+    const int pi = j >> 1, hs = j & 1;
+    const int64_t page = page_of(pi);
     const int64_t head_base = (page * L.Hkv + g) * head_elems;
-#pragma unroll 1
-    for (int hs = 0; hs < 2; ++hs) {
-      const int64_t kk0 = pk + 32 * hs;
-      if (kk0 >= k_end) break;
-      // ---- K operand (32 keys = 2 score blocks of 16) and S^T = K Q^T
-      f32x4_t sc[RB][2];
+    if (KV == BEAM_KV_BF16) {
+      const uint16_t* kb = static_cast<const uint16_t*>(C.k) + head_base;
+      const uint16_t* vb = static_cast<const uint16_t*>(C.v) + head_base + (int64_t)(32 * hs) * kHeadDim;
 #pragma unroll
-      for (int sb = 0; sb < 2; ++sb) {
-        const int krow = 32 * hs + 16 * sb + lc;       // key row inside the page
-        bf16x8_t kop[4];
-        if (KV == BEAM_KV_BF16) {
-          const uint16_t* kp = static_cast<const uint16_t*>(C.k) + head_base + (int64_t)krow * kHeadDim;
+      for (int sb = 0; sb < 2; ++sb)
 #pragma unroll
-          for (int i = 0; i < 4; ++i)
-            kop[i] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(kp + dslice<KV>(i, lg)));
-        } else {
-          const uint8_t* kp = static_cast<const uint8_t*>(C.k) + head_base + (int64_t)krow * kHeadDim;
+        for (int i = 0; i < 4; ++i)
+          kr[4 * sb + i] = *reinterpret_cast<const u32x4_t*>(
+              kb + (int64_t)(32 * hs + 16 * sb + lc) * kHeadDim + dslice<KV>(i, lg));
 #pragma unroll
-          for (int j = 0; j < 2; ++j) {
-            const u32x4_t w = *reinterpret_cast<const u32x4_t*>(kp + 64 * j + 16 * lg);
-            kop[2 * j] = fp8x8_to_bf16x8(w[0], w[1]);
-            kop[2 * j + 1] = fp8x8_to_bf16x8(w[2], w[3]);
-          }
-        }
+      for (int it = 0; it < 8; ++it)
+        vr[it] = *reinterpret_cast<const u32x4_t*>(vb + (int64_t)(lane / 16 + 4 * it) * kHeadDim + lc * 8);
+    } else {
+      const uint8_t* kb = static_cast<const uint8_t*>(C.k) + head_base;
+      const uint8_t* vb = static_cast<const uint8_t*>(C.v) + head_base + (int64_t)(32 * hs) * kHeadDim;
 #pragma unroll
-        for (int rb = 0; rb < RB; ++rb) {
-          f32x4_t s = {0.f, 0.f, 0.f, 0.f};
+      for (int sb = 0; sb < 2; ++sb)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop[i], qop[rb][i], s, 0, 0, 0);
-          sc[rb][sb] = s;
-        }
-      }
-      // ---- stage V rows (row-major bf16) in this wave's LDS region; keys >= kv are
-      // zeroed so that their (zero) probabilities never meet NaN payloads
+        for (int jj = 0; jj < 2; ++jj)
+          kr[2 * sb + jj] = *reinterpret_cast<const u32x4_t*>(
+              kb + (int64_t)(32 * hs + 16 * sb + lc) * kHeadDim + 64 * jj + 16 * lg);
+#pragma unroll
+      for (int it = 0; it < 4; ++it)
+        vr[it] = *reinterpret_cast<const u32x4_t*>(vb + (int64_t)(lane / 8 + 8 * it) * kHeadDim + (lane % 8) * 16);
+    }
+  };
+
+  auto compute = [&](const u32x4_t* kreg, const u32x4_t* vreg, int j) {
+    const int64_t kk0 = first_pk + (int64_t)kDecodeKeysPerBlockStep * (j >> 1) + 32 * (j & 1);
+    // ---- S^T = K Q^T (32 keys = 2 score blocks of 16)
+    f32x4_t sc[RB][2];
+#pragma unroll
+    for (int sb = 0; sb < 2; ++sb) {
+      bf16x8_t kop[4];
       if (KV == BEAM_KV_BF16) {
-        const uint16_t* vp = static_cast<const uint16_t*>(C.v) + head_base + (int64_t)(32 * hs) * kHeadDim;
 #pragma unroll
-        for (int it = 0; it < 8; ++it) {
-          const int r = lane / 16 + 4 * it;
-          u32x4_t w = *reinterpret_cast<const u32x4_t*>(vp + (int64_t)r * kHeadDim + lc * 8);
-          if (kk0 + r >= kv) w = u32x4_t{0u, 0u, 0u, 0u};
-          *reinterpret_cast<u32x4_t*>(vlds + r * kVRowBytes + lc * 16) = w;
-        }
+        for (int i = 0; i < 4; ++i) kop[i] = __builtin_bit_cast(bf16x8_t, kreg[4 * sb + i]);
       } else {
-        const uint8_t* vp = static_cast<const uint8_t*>(C.v) + head_base + (int64_t)(32 * hs) * kHeadDim;
 #pragma unroll
-        for (int it = 0; it < 4; ++it) {
-          const int r = lane / 8 + 8 * it;
-          const int cc = lane % 8;
-          u32x4_t w = *reinterpret_cast<const u32x4_t*>(vp + (int64_t)r * kHeadDim + cc * 16);
-          if (kk0 + r >= kv) w = u32x4_t{0u, 0u, 0u, 0u};
-          const bf16x8_t lo8 = fp8x8_to_bf16x8(w[0], w[1]);
-          const bf16x8_t hi8 = fp8x8_to_bf16x8(w[2], w[3]);
-          *reinterpret_cast<bf16x8_t*>(vlds + r * kVRowBytes + cc * 32) = lo8;
-          *reinterpret_cast<bf16x8_t*>(vlds + r * kVRowBytes + cc * 32 + 16) = hi8;
+        for (int jj = 0; jj < 2; ++jj) {
+          const u32x4_t w = kreg[2 * sb + jj];
+          kop[2 * jj] = fp8x8_to_bf16x8(w[0], w[1]);
+          kop[2 * jj + 1] = fp8x8_to_bf16x8(w[2], w[3]);
         }
       }
-      // ---- mask, online softmax, P^T as bf16 (k-slot order: block 0 keys 4lg..4lg+3,
-      // then block 1 keys 16+4lg..)
-      const bool need_mask = (kk0 + 31 > all_hi) || (kk0 < all_lo);
-      bf16x8_t pop[RB];
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb) {
-        float sv[8];
+        f32x4_t sacc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop[i], qop[rb][i], sacc, 0, 0, 0);
+        sc[rb][sb] = sacc;
+      }
+    }
+    // ---- stage V rows (row-major bf16) in this wave's LDS region; keys >= kv are
+    // zeroed so that their (zero) probabilities never meet NaN payloads
+    if (KV == BEAM_KV_BF16) {
+#pragma unroll
+      for (int it = 0; it < 8; ++it) {
+        const int r = lane / 16 + 4 * it;
+        u32x4_t w = vreg[it];
+        if (kk0 + r >= kv) w = u32x4_t{0u, 0u, 0u, 0u};
+        *reinterpret_cast<u32x4_t*>(vlds + r * kVRowBytes + lc * 16) = w;
+      }
+    } else {
+#pragma unroll
+      for (int it = 0; it < 4; ++it) {
+        const int r = lane / 8 + 8 * it;
+        const int cc = lane % 8;
+        u32x4_t w = vreg[it];
+        if (kk0 + r >= kv) w = u32x4_t{0u, 0u, 0u, 0u};
+        *reinterpret_cast<bf16x8_t*>(vlds + r * kVRowBytes + cc * 32) = fp8x8_to_bf16x8(w[0], w[1]);
+        *reinterpret_cast<bf16x8_t*>(vlds + r * kVRowBytes + cc * 32 + 16) = fp8x8_to_bf16x8(w[2], w[3]);
+      }
+    }
+    // ---- mask, online softmax, P^T as bf16 (k-slot order: block 0 keys 4lg..4lg+3,
+    // then block 1 keys 16+4lg..)
+    const bool need_mask = (kk0 + 31 > all_hi) || (kk0 < all_lo);
+    bf16x8_t pop[RB];
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      float sv[8];
+#pragma unroll
+      for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) sv[4 * sb + v] = sc[rb][sb][v];
+      if (need_mask) {
 #pragma unroll
         for (int sb = 0; sb < 2; ++sb)
 #pragma unroll
-          for (int v = 0; v < 4; ++v) sv[4 * sb + v] = sc[rb][sb][v];
-        if (need_mask) {
-#pragma unroll
-          for (int sb = 0; sb < 2; ++sb)
-#pragma unroll
-            for (int v = 0; v < 4; ++v) {
-              const int64_t j = kk0 + 16 * sb + 4 * lg + v;
-              if (j > row_pos[rb] || j < row_lo[rb]) sv[4 * sb + v] = -INFINITY;
-            }
-        }
-        float mx = sv[0];
-#pragma unroll
-        for (int e = 1; e < 8; ++e) mx = fmaxf(mx, sv[e]);
-        mx = wave_xor_max(mx, 16);
-        mx = wave_xor_max(mx, 32);
-        const float m_new = fmaxf(m_run[rb], mx * c);
-        const float m_use = m_new == -INFINITY ? 0.f : m_new;
-        const float alpha = exp2f(m_run[rb] - m_use);
-        float psum = 0.f;
-        float p[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          p[e] = exp2f(fmaf(sv[e], c, -m_use));
-          psum += p[e];
-        }
-        l_run[rb] = l_run[rb] * alpha + psum;
-        m_run[rb] = m_new;
-#pragma unroll
-        for (int d = 0; d < 8; ++d) acc[rb][d] *= alpha;
-        bf16x8_t pb;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) pb[e] = (__bf16)p[e];
-        pop[rb] = pb;
+          for (int v = 0; v < 4; ++v) {
+            const int64_t jk = kk0 + 16 * sb + 4 * lg + v;
+            if (jk > row_pos[rb] || jk < row_lo[rb]) sv[4 * sb + v] = -INFINITY;
+          }
       }
-      // ---- O^T += V^T P^T, V^T via transposing LDS reads
+      float mx = sv[0];
 #pragma unroll
-      for (int db = 0; db < 8; ++db) {
-        const int col = 16 * db + 4 * (lc % 4);
-        const unsigned char* a0 = vlds + (4 * lg + lc / 4) * kVRowBytes + col * 2;
-        const unsigned char* a1 = vlds + (16 + 4 * lg + lc / 4) * kVRowBytes + col * 2;
-        const i16x4_t t0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (__attribute__((address_space(3))) i16x4_t*)(a0));
-        const i16x4_t t1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (__attribute__((address_space(3))) i16x4_t*)(a1));
-        const u32x2_t u0 = __builtin_bit_cast(u32x2_t, t0), u1 = __builtin_bit_cast(u32x2_t, t1);
-        const u32x4_t uv = {u0[0], u0[1], u1[0], u1[1]};
-        const bf16x8_t vop = __builtin_bit_cast(bf16x8_t, uv);
+      for (int e = 1; e < 8; ++e) mx = fmaxf(mx, sv[e]);
+      mx = wave_xor_max(mx, 16);
+      mx = wave_xor_max(mx, 32);
+      const float m_new = fmaxf(m_run[rb], mx * c);
+      const float m_use = m_new == -INFINITY ? 0.f : m_new;
+      const float alpha = __builtin_amdgcn_exp2f(m_run[rb] - m_use);
+      float psum = 0.f;
+      bf16x8_t pb;
 #pragma unroll
-        for (int rb = 0; rb < RB; ++rb)
-          acc[rb][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, pop[rb], acc[rb][db], 0, 0, 0);
+      for (int e = 0; e < 8; ++e) {
+        const float pe = __builtin_amdgcn_exp2f(fmaf(sv[e], c, -m_use));
+        psum += pe;
+        pb[e] = (__bf16)pe;
       }
+      l_run[rb] = l_run[rb] * alpha + psum;
+      m_run[rb] = m_new;
+#pragma unroll
+      for (int d = 0; d < 8; ++d) acc[rb][d] *= alpha;
+      pop[rb] = pb;
     }
+    // ---- O^T += V^T P^T, V^T via transposing LDS reads
+#pragma unroll
+    for (int db = 0; db < 8; ++db) {
+      const int col = 16 * db + 4 * (lc % 4);
+      const unsigned char* a0 = vlds + (4 * lg + lc / 4) * kVRowBytes + col * 2;
+      const unsigned char* a1 = vlds + (16 + 4 * lg + lc / 4) * kVRowBytes + col * 2;
+      const i16x4_t t0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (__attribute__((address_space(3))) i16x4_t*)(a0));
+      const i16x4_t t1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (__attribute__((address_space(3))) i16x4_t*)(a1));
+      const u32x2_t u0 = __builtin_bit_cast(u32x2_t, t0), u1 = __builtin_bit_cast(u32x2_t, t1);
+      const u32x4_t uv = {u0[0], u0[1], u1[0], u1[1]};
+      const bf16x8_t vop = __builtin_bit_cast(bf16x8_t, uv);
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb)
+        acc[rb][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, pop[rb], acc[rb][db], 0, 0, 0);
+    }
+  };
+
+  // ping-pong between two register sets: fetch the next half-step, compute this one
+  if (n_half > 0) fetch(0, kreg, vreg);
+#pragma unroll 1
+  for (int j = 0; j < n_half; j += 2) {
+    if (j + 1 < n_half) fetch(j + 1, kreg_n, vreg_n);
+    compute(kreg, vreg, j);
+    if (j + 1 >= n_half) break;
+    if (j + 2 < n_half) fetch(j + 2, kreg, vreg);
+    compute(kreg_n, vreg_n, j + 1);
   }
 
   // ---- merge the 4 waves of this workgroup (LDS), then write
@@ -338,45 +391,65 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(
   }
 }
 
-// Log-sum-exp merge of the split partials of each (token, head), then the gate.
+// Log-sum-exp merge of the split partials of each (token, head) row, then the gate.
+// One 256-thread workgroup per row: the 4 waves take splits w, w+4, ... with independent
+// loads in flight, each lane owning 2 of the 128 output dims; the waves then combine in
+// a fixed order through LDS.
 __global__ __launch_bounds__(256) void decode_merge_kernel(
     LayerParams L, BatchParams B, DecodeSplit S, const float* __restrict__ ws_o,
     const float* __restrict__ ws_ml, int64_t ws_rows, const uint16_t* __restrict__ gate,
     int64_t gate_stride, const uint16_t* __restrict__ gate_bias, uint16_t* out,
     int64_t out_stride) {
-  const int64_t tok = blockIdx.x;
+  __shared__ float s_red[4];
+  __shared__ float s_o[4][kHeadDim];
+  __shared__ float s_l[4];
+  const int64_t row = blockIdx.x;                 // tok * Hq + h
+  const int64_t tok = row / L.Hq;
+  const int h = (int)(row % L.Hq);
   const int wave = threadIdx.x / 64, lane = threadIdx.x % 64;
   const int b = seq_of_token(B.q_start, B.num_seqs, tok);
   const int64_t n = (int64_t)B.q_start[b + 1] - B.q_start[b];
   const int64_t kv = B.kv_len[b];
   const int64_t base = range_base(L, kv, n);
   const int used = (int)((kv - base + S.keys_per_split - 1) / S.keys_per_split);
-  for (int h = wave; h < L.Hq; h += 4) {
-    const int64_t row = tok * L.Hq + h;
-    float M = -INFINITY;
-    for (int s = 0; s < used; ++s) M = fmaxf(M, ws_ml[((int64_t)s * ws_rows + row) * 2]);
-    float lsum = 0.f, o0 = 0.f, o1 = 0.f;
-    for (int s = 0; s < used; ++s) {
-      const int64_t wrow = (int64_t)s * ws_rows + row;
-      const float ms = ws_ml[wrow * 2];
-      if (ms == -INFINITY) continue;
-      const float w = exp2f(ms - M);
-      lsum += w * ws_ml[wrow * 2 + 1];
-      const float2 o = *reinterpret_cast<const float2*>(ws_o + wrow * kHeadDim + 2 * lane);
-      o0 += w * o.x;
-      o1 += w * o.y;
-    }
-    const float inv = lsum > 0.f ? 1.0f / lsum : 0.f;
-    float y0 = o0 * inv, y1 = o1 * inv;
-    const int d = 2 * lane;
-    if (gate != nullptr) {
-      const uint32_t gw = *reinterpret_cast<const uint32_t*>(gate + tok * gate_stride + (int64_t)h * kHeadDim + d);
-      const float bh = bf16_to_f32(gate_bias[h]);
-      y0 *= 1.0f / (1.0f + expf(-(bf16_to_f32(gw & 0xFFFFu) + bh)));
-      y1 *= 1.0f / (1.0f + expf(-(bf16_to_f32(gw >> 16) + bh)));
-    }
-    *reinterpret_cast<uint32_t*>(out + tok * out_stride + (int64_t)h * kHeadDim + d) = pack_bf16x2(y0, y1);
+
+  float M = -INFINITY;
+  for (int s = threadIdx.x; s < used; s += 256) M = fmaxf(M, ws_ml[((int64_t)s * ws_rows + row) * 2]);
+  for (int o = 32; o >= 1; o >>= 1) M = fmaxf(M, __shfl_xor(M, o, 64));
+  if (lane == 0) s_red[wave] = M;
+  __syncthreads();
+  M = fmaxf(fmaxf(s_red[0], s_red[1]), fmaxf(s_red[2], s_red[3]));
+
+  float lsum = 0.f, o0 = 0.f, o1 = 0.f;
+#pragma unroll 4
+  for (int s = wave; s < used; s += 4) {
+    const int64_t wrow = (int64_t)s * ws_rows + row;
+    const float2 ml = *reinterpret_cast<const float2*>(ws_ml + wrow * 2);
+    const float2 o = *reinterpret_cast<const float2*>(ws_o + wrow * kHeadDim + 2 * lane);
+    const float w = ml.x == -INFINITY ? 0.f : exp2f(ml.x - M);
+    lsum += w * ml.y;
+    o0 += w * o.x;
+    o1 += w * o.y;
   }
+  s_o[wave][2 * lane] = o0;
+  s_o[wave][2 * lane + 1] = o1;
+  if (lane == 0) s_l[wave] = lsum;
+  __syncthreads();
+  if (wave != 0) return;
+  const float ltot = ((s_l[0] + s_l[1]) + s_l[2]) + s_l[3];
+  const int d = 2 * lane;
+  float y0 = ((s_o[0][d] + s_o[1][d]) + s_o[2][d]) + s_o[3][d];
+  float y1 = ((s_o[0][d + 1] + s_o[1][d + 1]) + s_o[2][d + 1]) + s_o[3][d + 1];
+  const float inv = ltot > 0.f ? 1.0f / ltot : 0.f;
+  y0 *= inv;
+  y1 *= inv;
+  if (gate != nullptr) {
+    const uint32_t gw = *reinterpret_cast<const uint32_t*>(gate + tok * gate_stride + (int64_t)h * kHeadDim + d);
+    const float bh = bf16_to_f32(gate_bias[h]);
+    y0 *= 1.0f / (1.0f + expf(-(bf16_to_f32(gw & 0xFFFFu) + bh)));
+    y1 *= 1.0f / (1.0f + expf(-(bf16_to_f32(gw >> 16) + bh)));
+  }
+  *reinterpret_cast<uint32_t*>(out + tok * out_stride + (int64_t)h * kHeadDim + d) = pack_bf16x2(y0, y1);
 }
 
 template <int KV>
@@ -401,7 +474,7 @@ hipError_t launch_kv(const LayerParams& L, const BatchParams& B, const CachePara
 #undef BEAM_DECODE_LAUNCH
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || S.num_splits == 1) return e;
-  hipLaunchKernelGGL(decode_merge_kernel, dim3((unsigned)B.num_tokens), dim3(256), 0, stream, L,
+  hipLaunchKernelGGL(decode_merge_kernel, dim3((unsigned)(B.num_tokens * L.Hq)), dim3(256), 0, stream, L,
                      B, S, ws_o, ws_ml, ws_rows, static_cast<const uint16_t*>(gate), gate_stride,
                      static_cast<const uint16_t*>(gate_bias), static_cast<uint16_t*>(out),
                      out_stride);

@@ -45,6 +45,7 @@ __device__ __forceinline__ float swap_halves_sum(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+template <int KIND>
 __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(
     LayerParams L, BatchParams B, CacheParams C, const uint16_t* __restrict__ q, int64_t q_stride,
     const uint16_t* __restrict__ gate, int64_t gate_stride, const uint16_t* __restrict__ gate_bias,
@@ -67,7 +68,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(
   if (n <= 0 || tile_row0 >= rows_b) return;
   const int64_t kv = B.kv_len[b];
   const int64_t first_pos = kv - n;
-  const bool swa = L.kind == BEAM_LAYER_SWA;
+  constexpr bool swa = KIND == BEAM_LAYER_SWA;
   const int64_t tile_rows = rows_b - tile_row0 < kRowsPerBlock ? rows_b - tile_row0 : kRowsPerBlock;
 
   // key range of the workgroup
@@ -290,11 +291,14 @@ hipError_t launch_attn_prefill(const LayerParams& L, const BatchParams& B, const
   if (B.num_tokens == 0 || B.num_seqs == 0 || B.max_q_len == 0) return hipSuccess;
   const int64_t tiles = ((int64_t)B.max_q_len * L.G + kRowsPerBlock - 1) / kRowsPerBlock;
   const dim3 grid((unsigned)tiles, (unsigned)L.Hkv, (unsigned)B.num_seqs), block(kThreads);
-  hipLaunchKernelGGL(prefill_kernel, grid, block, 0, stream, L, B, C,
-                     static_cast<const uint16_t*>(q), q_stride,
-                     static_cast<const uint16_t*>(gate), gate_stride,
-                     static_cast<const uint16_t*>(gate_bias), static_cast<uint16_t*>(out),
-                     out_stride);
+  auto launch = [&](auto kernel) {
+    hipLaunchKernelGGL(kernel, grid, block, 0, stream, L, B, C, static_cast<const uint16_t*>(q),
+                       q_stride, static_cast<const uint16_t*>(gate), gate_stride,
+                       static_cast<const uint16_t*>(gate_bias), static_cast<uint16_t*>(out),
+                       out_stride);
+  };
+  if (L.kind == BEAM_LAYER_SWA) launch(prefill_kernel<BEAM_LAYER_SWA>);
+  else launch(prefill_kernel<BEAM_LAYER_FULL>);
   return hipGetLastError();
 }
 
