@@ -12,27 +12,43 @@
 //    a workgroup owns 256 consecutive rows (about 43 tokens x 6 heads), so every K/V
 //    tile it stages in LDS serves all 6 query heads of the group (GQA reuse) and all of
 //    its tokens. Grid: (row tile, KV head, sequence).
-//  * 4 waves x 64 rows; a wave computes S^T = K Q^T with MFMA 32x32x16 bf16 for two
-//    32-row blocks that share each K operand read from LDS. After the MFMA, a lane holds
-//    32 scores of one row, so the row max/sum need one cross-half swap (permlane32).
-//  * O^T = V^T P^T: P^T is the score accumulator packed to bf16 in place (the key order
-//    of the accumulator is the MFMA's k-slot order); V^T is read from the row-major V
-//    tile with the gfx950 transposing LDS read ds_read_b64_tr_b16.
-//  * K/V tiles are one 64-token page per KV head (16 KiB each), double-buffered in LDS;
-//    the next page is fetched into registers while the current one is consumed.
-//  * Fully visible tiles skip the mask; tiles wholly outside a wave's rows are skipped.
+//  * K/V tiles are one 64-token page of one KV head (16 KiB each), copied straight from
+//    global memory into LDS with gfx950's global_load_lds_dwordx4 (no staging registers)
+//    and double-buffered: the next page is in flight while the current one is consumed.
+//    Each 256-byte row is stored with its 16-byte chunks XOR-swizzled by the row index so
+//    that the operand reads below hit distinct LDS banks.
+//  * 4 waves x 64 rows. Per 32-key half of a tile a wave computes S^T = K Q^T with MFMA
+//    32x32x16 bf16 for two 32-row blocks sharing each K operand; a lane then holds 16
+//    scores of one row, so row max/sum take one cross-half swap (permlane32).
+//  * O^T += V^T P^T: P^T is the score accumulator packed to bf16 in place (its key order
+//    is the MFMA's k-slot order); V^T comes from the row-major V tile through the
+//    transposing LDS read ds_read_b64_tr_b16.
+//  * The running maximum is only raised when a row's maximum grows by more than 2^8
+//    (log2 domain), so the 128-value output rescale is skipped on almost every tile;
+//    the final division by the same running sum keeps the result exact.
+//  * Fully visible tiles skip the mask; tiles wholly outside a wave's rows skip compute.
+#include <type_traits>
+
 #include "beam_common.h"
 
 namespace beam {
 namespace {
 
-constexpr int kWaves = 4;
+// Workgroup shape: RB 32-row MFMA blocks per wave, WAVES waves, 256 rows in all.
+constexpr int kRowsPerBlock = 256;
+constexpr int kRB = 1;                                   // 32 rows per wave ...
+constexpr int kWaves = kRowsPerBlock / (32 * kRB);       // ... 8 waves, 2 per SIMD
 constexpr int kThreads = kWaves * 64;
-constexpr int kRowsPerWave = 64;
-constexpr int kRowsPerBlock = kWaves * kRowsPerWave;     // 256
-constexpr int kRowBytes = kHeadDim * 2 + 16;             // padded LDS row (bf16)
-constexpr int kTileBytes = kPage * kRowBytes;            // one K or V page tile
+constexpr int kRowsPerWave = 32 * kRB;
+constexpr int kRowBytes = kHeadDim * 2;                  // 256-byte bf16 row, swizzled chunks
+constexpr int kTileBytes = kPage * kRowBytes;            // one K or V page tile: 16 KiB
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kRescaleSlack = 8.0f;                    // log2 headroom before rescaling
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+// byte offset of 16-byte chunk `c` (0..15) of row `r` inside a swizzled tile
+__device__ __forceinline__ int swz(int r, int c) { return r * kRowBytes + ((c ^ (r & 15)) << 4); }
 
 __device__ __forceinline__ float swap_halves_max(float x) {
   const uint32_t u = __float_as_uint(x);
@@ -46,11 +62,11 @@ __device__ __forceinline__ float swap_halves_sum(float x) {
 }
 
 template <int KIND>
-__global__ __launch_bounds__(kThreads, 1) void prefill_kernel(
+__global__ __launch_bounds__(kThreads) void prefill_kernel(
     LayerParams L, BatchParams B, CacheParams C, const uint16_t* __restrict__ q, int64_t q_stride,
     const uint16_t* __restrict__ gate, int64_t gate_stride, const uint16_t* __restrict__ gate_bias,
     uint16_t* out, int64_t out_stride) {
-  __shared__ __attribute__((aligned(16))) unsigned char lds[2 * 2 * kTileBytes];
+  __shared__ __attribute__((aligned(1024))) unsigned char lds[2 * 2 * kTileBytes];
 
   const int tile = blockIdx.x;
   const int g = blockIdx.y;
@@ -60,45 +76,45 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(
   const int lane = tid % 64;
   const int half = lane / 32;      // which 8-slice of each 16-wide k step this lane feeds
   const int lr = lane % 32;        // the row (within a 32-row block) this lane owns
-
-  const int64_t q0 = B.q_start[b];
-  const int64_t n = (int64_t)B.q_start[b + 1] - q0;
-  const int64_t rows_b = n * L.G;
-  const int64_t tile_row0 = (int64_t)tile * kRowsPerBlock;
-  if (n <= 0 || tile_row0 >= rows_b) return;
-  const int64_t kv = B.kv_len[b];
-  const int64_t first_pos = kv - n;
   constexpr bool swa = KIND == BEAM_LAYER_SWA;
-  const int64_t tile_rows = rows_b - tile_row0 < kRowsPerBlock ? rows_b - tile_row0 : kRowsPerBlock;
 
-  // key range of the workgroup
-  const int64_t pos_first = first_pos + tile_row0 / L.G;
-  const int64_t pos_last = first_pos + (tile_row0 + tile_rows - 1) / L.G;
-  const int64_t key_lo = swa ? (pos_first - L.window + 1 > 0 ? pos_first - L.window + 1 : 0) : 0;
-  const int64_t kt_begin = key_lo / kPage;
-  const int64_t kt_end = pos_last / kPage + 1;            // exclusive
+  const int q0 = B.q_start[b];
+  const int n = B.q_start[b + 1] - q0;
+  const int rows_b = n * L.G;
+  const int tile_row0 = tile * kRowsPerBlock;
+  if (n <= 0 || tile_row0 >= rows_b) return;
+  const int kv = B.kv_len[b];
+  const int first_pos = kv - n;
+  const int tile_rows = rows_b - tile_row0 < kRowsPerBlock ? rows_b - tile_row0 : kRowsPerBlock;
+
+  // key range of the workgroup, in 64-key tiles
+  const int pos_first = first_pos + tile_row0 / L.G;
+  const int pos_last = first_pos + (tile_row0 + tile_rows - 1) / L.G;
+  const int key_lo = swa ? max(pos_first - L.window + 1, 0) : 0;
+  const int kt_begin = key_lo / kPage;
+  const int kt_end = pos_last / kPage + 1;               // exclusive
 
   // rows of this wave
-  const int64_t wrow0 = tile_row0 + wave * kRowsPerWave;
-  const int64_t wrows = tile_row0 + tile_rows - wrow0;    // may be <= 0
+  const int wrow0 = tile_row0 + wave * kRowsPerWave;
+  const int wrows = min(tile_row0 + tile_rows - wrow0, kRowsPerWave);   // may be <= 0
   const bool wave_active = wrows > 0;
-  const int64_t w_min_pos = first_pos + (wave_active ? wrow0 / L.G : 0);
-  const int64_t w_max_pos = first_pos + (wave_active ? (wrow0 + (wrows < kRowsPerWave ? wrows : kRowsPerWave) - 1) / L.G : -1);
-  const int64_t w_max_lo = swa ? (w_max_pos - L.window + 1 > 0 ? w_max_pos - L.window + 1 : 0) : 0;
-  const int64_t w_min_lo = swa ? (w_min_pos - L.window + 1 > 0 ? w_min_pos - L.window + 1 : 0) : 0;
+  const int w_min_pos = wave_active ? first_pos + wrow0 / L.G : 0;
+  const int w_max_pos = wave_active ? first_pos + (wrow0 + wrows - 1) / L.G : -1;
+  const int w_max_lo = swa ? max(w_max_pos - L.window + 1, 0) : 0;
+  const int w_min_lo = swa ? max(w_min_pos - L.window + 1, 0) : 0;
 
   // per-lane rows: Q^T operand, position, window start
-  bf16x8_t qop[2][8];
-  int64_t row_pos[2], row_lo[2];
+  bf16x8_t qop[kRB][8];
+  int row_pos[kRB], row_lo[kRB];
 #pragma unroll
-  for (int rb = 0; rb < 2; ++rb) {
-    const int64_t r = wrow0 + 32 * rb + lr;
+  for (int rb = 0; rb < kRB; ++rb) {
+    const int r = wrow0 + 32 * rb + lr;
     const bool valid = wave_active && (r - wrow0) < wrows;
-    const int64_t t = valid ? r / L.G : 0;
-    const int h = g * L.G + (int)(valid ? r % L.G : 0);
+    const int t = valid ? r / L.G : 0;
+    const int h = g * L.G + (valid ? r % L.G : 0);
     row_pos[rb] = valid ? first_pos + t : -1;
-    row_lo[rb] = (swa && valid) ? (row_pos[rb] - L.window + 1 > 0 ? row_pos[rb] - L.window + 1 : 0) : 0;
-    const uint16_t* qrow = q + (q0 + t) * q_stride + (int64_t)h * kHeadDim;
+    row_lo[rb] = (swa && valid) ? max(row_pos[rb] - L.window + 1, 0) : 0;
+    const uint16_t* qrow = q + (int64_t)(q0 + t) * q_stride + (int64_t)h * kHeadDim;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       u32x4_t v = {0u, 0u, 0u, 0u};
@@ -108,155 +124,172 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(
   }
 
   const float c = L.sm_scale * kLog2e;
-  float m_run[2] = {-INFINITY, -INFINITY};
-  float l_run[2] = {0.f, 0.f};
-  f32x16_t acc[2][4];
+  float m_run[kRB], l_run[kRB];
+  f32x16_t acc[kRB][4];
 #pragma unroll
-  for (int rb = 0; rb < 2; ++rb)
+  for (int rb = 0; rb < kRB; ++rb) {
+    m_run[rb] = -INFINITY;
+    l_run[rb] = 0.f;
 #pragma unroll
     for (int db = 0; db < 4; ++db)
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[rb][db][e] = 0.f;
+  }
 
-  // ---- global -> register staging of one K and one V page tile (4 x 16 B each per thread)
-  const uint16_t* kcache = static_cast<const uint16_t*>(C.k);
-  const uint16_t* vcache = static_cast<const uint16_t*>(C.v);
-  const int st_row = tid / 16;          // + 16 * it
-  const int st_col = (tid % 16) * 8;    // elements
-  u32x4_t stage_k[4], stage_v[4];
-  auto fetch = [&](int64_t kt) {
-    const int64_t page = B.block_table[(int64_t)b * B.max_pages + kt];
-    const int64_t base = (page * L.Hkv + g) * (int64_t)kPage * kHeadDim;
+  // ---- direct global -> LDS copy of one K and one V page tile. Wave w copies rows
+  // [w*R, w*R + R) of each (R = 64 / waves): R/4 instructions per tensor, each 64 lanes
+  // x 16 bytes = 4 rows.
+  // Lane l writes LDS bytes [16 l, 16 l + 16) of its 1 KiB block, i.e. row 4i + l/16,
+  // chunk slot l%16, which holds the row's chunk (l%16) ^ (row & 15).
+  const char* kcache = static_cast<const char*>(C.k);
+  const char* vcache = static_cast<const char*>(C.v);
+  const int32_t* bt_row = B.block_table + (int64_t)b * B.max_pages;
+  auto issue_tile = [&](int kt, int buf) {
+    const int64_t page = bt_row[kt];
+    const int64_t base = (page * L.Hkv + g) * (int64_t)kTileBytes;
+    unsigned char* kl = lds + buf * 2 * kTileBytes;
+    unsigned char* vl = kl + kTileBytes;
+    constexpr int kRowsCopied = kPage / kWaves;
 #pragma unroll
-    for (int it = 0; it < 4; ++it) {
-      const int r = st_row + 16 * it;
-      const int64_t off = base + (int64_t)r * kHeadDim + st_col;
-      stage_k[it] = *reinterpret_cast<const u32x4_t*>(kcache + off);
-      stage_v[it] = *reinterpret_cast<const u32x4_t*>(vcache + off);
-      if (kt * kPage + r >= kv) {   // slots past the sequence may hold NaN
-        stage_k[it] = u32x4_t{0u, 0u, 0u, 0u};
-        stage_v[it] = u32x4_t{0u, 0u, 0u, 0u};
-      }
-    }
-  };
-  auto commit = [&](int buf) {
-    unsigned char* kt_lds = lds + buf * 2 * kTileBytes;
-    unsigned char* vt_lds = kt_lds + kTileBytes;
-#pragma unroll
-    for (int it = 0; it < 4; ++it) {
-      const int r = st_row + 16 * it;
-      *reinterpret_cast<u32x4_t*>(kt_lds + r * kRowBytes + st_col * 2) = stage_k[it];
-      *reinterpret_cast<u32x4_t*>(vt_lds + r * kRowBytes + st_col * 2) = stage_v[it];
+    for (int i = 0; i < kRowsCopied / 4; ++i) {
+      const int row = kRowsCopied * wave + 4 * i + lane / 16;
+      const int chunk = (lane % 16) ^ (row & 15);
+      const int64_t src = base + row * kRowBytes + chunk * 16;
+      const int dst = (kRowsCopied * wave + 4 * i) * kRowBytes;  // wave-uniform block start
+      __builtin_amdgcn_global_load_lds(kcache + src, (lds_void_t*)(kl + dst), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(vcache + src, (lds_void_t*)(vl + dst), 16, 0, 0);
     }
   };
 
-  fetch(kt_begin);
-  commit(0);
+  issue_tile(kt_begin, 0);
+  __builtin_amdgcn_s_waitcnt(0);       // vmcnt(0) lgkmcnt(0): this wave's copies landed
   __syncthreads();
 
-  for (int64_t kt = kt_begin; kt < kt_end; ++kt) {
-    const int buf = (int)((kt - kt_begin) & 1);
-    const bool has_next = kt + 1 < kt_end;
-    if (has_next) fetch(kt + 1);
-    const int64_t k0 = kt * kPage;
+  const int grp = lane / 16, gi = lane % 16;
+  for (int kt = kt_begin; kt < kt_end; ++kt) {
+    const int buf = (kt - kt_begin) & 1;
+    if (kt + 1 < kt_end) issue_tile(kt + 1, buf ^ 1);
+    const int k0 = kt * kPage;
     const bool skip = !wave_active || k0 > w_max_pos || k0 + kPage - 1 < w_min_lo;
     if (!skip) {
-      const unsigned char* kt_lds = lds + buf * 2 * kTileBytes;
-      const unsigned char* vt_lds = kt_lds + kTileBytes;
-      // ---- S^T = K Q^T for 2 key blocks x 2 row blocks
-      f32x16_t sc[2][2];
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-        for (int rb = 0; rb < 2; ++rb)
-#pragma unroll
-          for (int e = 0; e < 16; ++e) sc[kb][rb][e] = 0.f;
-        const unsigned char* krow = kt_lds + (32 * kb + lr) * kRowBytes + 16 * half;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const bf16x8_t kop = *reinterpret_cast<const bf16x8_t*>(krow + 32 * i);
-#pragma unroll
-          for (int rb = 0; rb < 2; ++rb)
-            sc[kb][rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop, qop[rb][i], sc[kb][rb], 0, 0, 0);
-        }
-      }
-      const bool need_mask = (k0 + kPage - 1 > w_min_pos) || (k0 < w_max_lo);
-      bf16x8_t pop[2][4];
-#pragma unroll
-      for (int rb = 0; rb < 2; ++rb) {
-        if (need_mask) {
-#pragma unroll
-          for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-            for (int v = 0; v < 16; ++v) {
-              const int64_t j = k0 + 32 * kb + (v / 4) * 8 + half * 4 + (v % 4);
-              if (j > row_pos[rb] || j < row_lo[rb]) sc[kb][rb][v] = -INFINITY;
+      // MASK: some key of the tile is invisible to some row of the wave; TAIL: the tile
+      // holds slots past the sequence end (they may hold NaN; a TAIL tile also masks)
+      auto compute = [&](auto mask_c, auto tail_c) {
+        constexpr bool MASK = decltype(mask_c)::value;
+        constexpr bool TAIL = decltype(tail_c)::value;
+        const unsigned char* kt_lds = lds + buf * 2 * kTileBytes;
+        const unsigned char* vt_lds = kt_lds + kTileBytes;
+  #pragma unroll 1
+        for (int kh = 0; kh < 2; ++kh) {         // 32-key halves of the tile
+          // ---- S^T = K Q^T for this half, two row blocks
+          f32x16_t sc[kRB];
+  #pragma unroll
+          for (int rb = 0; rb < kRB; ++rb)
+  #pragma unroll
+            for (int e = 0; e < 16; ++e) sc[rb][e] = 0.f;
+          const int krow = 32 * kh + lr;
+          __builtin_amdgcn_sched_barrier(0);
+          bf16x8_t kop[8];
+  #pragma unroll
+          for (int i = 0; i < 8; ++i)
+            kop[i] = *reinterpret_cast<const bf16x8_t*>(kt_lds + swz(krow, 2 * i + half));
+  #pragma unroll
+          for (int i = 0; i < 8; ++i)
+  #pragma unroll
+            for (int rb = 0; rb < kRB; ++rb)
+              sc[rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[i], qop[rb][i], sc[rb], 0, 0, 0);
+          __builtin_amdgcn_sched_barrier(0);
+          // ---- mask, online softmax, P^T in bf16
+          bf16x8_t pop[kRB][2];
+  #pragma unroll
+          for (int rb = 0; rb < kRB; ++rb) {
+            if (MASK) {
+  #pragma unroll
+              for (int v = 0; v < 16; ++v) {
+                const int j = k0 + 32 * kh + (v / 4) * 8 + half * 4 + (v % 4);
+                if (j > row_pos[rb] || j < row_lo[rb]) sc[rb][v] = -INFINITY;
+              }
             }
-        }
-        float mx = sc[0][rb][0];
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int v = 0; v < 16; ++v) mx = fmaxf(mx, sc[kb][rb][v]);
-        mx = swap_halves_max(mx);
-        const float m_new = fmaxf(m_run[rb], mx * c);
-        const float m_use = m_new == -INFINITY ? 0.f : m_new;
-        const float alpha = __builtin_amdgcn_exp2f(m_run[rb] - m_use);
-        float psum = 0.f;
-#pragma unroll
-        for (int cc = 0; cc < 4; ++cc) {
-          bf16x8_t pb;
-#pragma unroll
-          for (int j = 0; j < 8; ++j) {
-            const float p = __builtin_amdgcn_exp2f(fmaf(sc[cc / 2][rb][8 * (cc % 2) + j], c, -m_use));
-            psum += p;
-            pb[j] = (__bf16)p;
+            float mx = fmaxf(sc[rb][0], sc[rb][1]);
+  #pragma unroll
+            for (int v = 2; v < 16; ++v) mx = fmaxf(mx, sc[rb][v]);
+            mx = swap_halves_max(mx) * c;
+            // raise the running max only when it grew by more than the slack
+            if (__builtin_amdgcn_ballot_w64(mx > m_run[rb] + kRescaleSlack) != 0) {
+              const float m_new = fmaxf(m_run[rb], mx);
+              // 0 when this row saw no key before; 1 when it still sees none
+              const float alpha = m_new == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m_run[rb] - m_new);
+              l_run[rb] *= alpha;
+  #pragma unroll
+              for (int db = 0; db < 4; ++db) acc[rb][db] *= alpha;
+              m_run[rb] = m_new;
+            }
+            const float m_use = m_run[rb] == -INFINITY ? 0.f : m_run[rb];
+            float psum = 0.f;
+  #pragma unroll
+            for (int cc = 0; cc < 2; ++cc) {
+              bf16x8_t pb;
+  #pragma unroll
+              for (int jj = 0; jj < 8; ++jj) {
+                const float p = __builtin_amdgcn_exp2f(fmaf(sc[rb][8 * cc + jj], c, -m_use));
+                psum += p;
+                pb[jj] = (__bf16)p;
+              }
+              pop[rb][cc] = pb;
+            }
+            l_run[rb] += psum;
           }
-          pop[rb][cc] = pb;
+          __builtin_amdgcn_sched_barrier(0);
+          // ---- O^T += V^T P^T over the 32 keys of this half (2 MFMA k-steps of 16)
+  #pragma unroll
+          for (int cc = 0; cc < 2; ++cc) {
+            const int key0 = 32 * kh + 16 * cc + 4 * (grp / 2) + gi / 4;   // row read by this lane
+  #pragma unroll
+            for (int db = 0; db < 4; ++db) {
+              const int col = 32 * db + 16 * (grp % 2) + 4 * (gi % 4);    // bf16 element column
+              const int off0 = swz(key0, col / 8) + (col % 8) * 2;
+              const int off1 = swz(key0 + 8, col / 8) + (col % 8) * 2;
+              i16x4_t t0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                  (__attribute__((address_space(3))) i16x4_t*)(vt_lds + off0));
+              i16x4_t t1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                  (__attribute__((address_space(3))) i16x4_t*)(vt_lds + off1));
+              if (TAIL) {
+                // this lane received keys key0-(gi/4)+0..3 (t0) and +8 (t1) at one column
+                const int kb0 = k0 + 32 * kh + 16 * cc + 4 * (grp / 2);
+  #pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                  if (kb0 + e >= kv) t0[e] = 0;
+                  if (kb0 + 8 + e >= kv) t1[e] = 0;
+                }
+              }
+              const u32x2_t u0 = __builtin_bit_cast(u32x2_t, t0), u1 = __builtin_bit_cast(u32x2_t, t1);
+              const u32x4_t uv = {u0[0], u0[1], u1[0], u1[1]};
+              const bf16x8_t vop = __builtin_bit_cast(bf16x8_t, uv);
+  #pragma unroll
+              for (int rb = 0; rb < kRB; ++rb)
+                acc[rb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop, pop[rb][cc], acc[rb][db], 0, 0, 0);
+            }
+          }
         }
-        l_run[rb] = l_run[rb] * alpha + psum;
-        m_run[rb] = m_new;
-#pragma unroll
-        for (int db = 0; db < 4; ++db) acc[rb][db] *= alpha;
-      }
-      // ---- O^T += V^T P^T
-      const int grp = lane / 16, gi = lane % 16;
-      const int hh = grp / 2;
-#pragma unroll
-      for (int db = 0; db < 4; ++db) {
-        const int col = 32 * db + 16 * (grp % 2) + 4 * (gi % 4);
-#pragma unroll
-        for (int cc = 0; cc < 4; ++cc) {
-          const unsigned char* a0 = vt_lds + (16 * cc + 4 * hh + gi / 4) * kRowBytes + col * 2;
-          const unsigned char* a1 = a0 + 8 * kRowBytes;
-          const i16x4_t t0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (__attribute__((address_space(3))) i16x4_t*)(a0));
-          const i16x4_t t1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (__attribute__((address_space(3))) i16x4_t*)(a1));
-          const u32x2_t u0 = __builtin_bit_cast(u32x2_t, t0), u1 = __builtin_bit_cast(u32x2_t, t1);
-          const u32x4_t uv = {u0[0], u0[1], u1[0], u1[1]};
-          const bf16x8_t vop = __builtin_bit_cast(bf16x8_t, uv);
-#pragma unroll
-          for (int rb = 0; rb < 2; ++rb)
-            acc[rb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop, pop[rb][cc], acc[rb][db], 0, 0, 0);
-        }
-      }
+      };
+      const bool need_mask = (k0 + kPage - 1 > w_min_pos) || (k0 < w_max_lo);
+      if (k0 + kPage > kv) compute(std::true_type{}, std::true_type{});
+      else if (need_mask) compute(std::true_type{}, std::false_type{});
+      else compute(std::false_type{}, std::false_type{});
     }
-    if (has_next) {
-      commit(buf ^ 1);
-    }
-    __syncthreads();
+    __builtin_amdgcn_s_waitcnt(0);     // this wave's copies of the next tile landed
+    __syncthreads();                   // ... and everyone's; the current buffer is free
   }
 
   // ---- epilogue: 1/l, gate, bf16 store (lane owns row lr of each block; d values
   // 32*db + 8*(v/4) + 4*half + (v%4))
 #pragma unroll
-  for (int rb = 0; rb < 2; ++rb) {
+  for (int rb = 0; rb < kRB; ++rb) {
     const float lsum = swap_halves_sum(l_run[rb]);
-    const int64_t r = wrow0 + 32 * rb + lr;
+    const int r = wrow0 + 32 * rb + lr;
     if (!wave_active || (r - wrow0) >= wrows) continue;
-    const int64_t t = r / L.G;
-    const int h = g * L.G + (int)(r % L.G);
+    const int t = r / L.G;
+    const int h = g * L.G + r % L.G;
     const int64_t tok = q0 + t;
     const float inv = lsum > 0.f ? 1.0f / lsum : 0.f;
     const float bh = gate != nullptr ? bf16_to_f32(gate_bias[h]) : 0.f;
