@@ -167,6 +167,57 @@ def seq0_host_inputs(call, rows_wanted):
     return inp, rows
 
 
+def run_decode(args, result):
+    """The decode / verify workloads: batch-1 decode at p = 100,000 (bf16), 32 sequences
+    of 8K..128K keys (fp8), and an 8-token verify block on 1,048,576 keys (fp8); each as
+    a full NoPE layer and an SWA-512 layer (fused norm + KV store, then split-K decode
+    attention with the gate)."""
+    import torch
+
+    import synth
+    from nope_gqa_attention_amd import beamattn as ba
+
+    dec = {}
+    for cfg in (2, 3, 4):
+        for kind in ("full", "swa"):
+            call = synth.make_config(cfg, kind, cache_device="cuda")
+            s = Staged(call)
+            ql = [int(x) for x in call.q_lens]
+            kl = [int(x) for x in call.kv_len]
+            copies = [s]
+            if cfg == 2 and kind == "full":
+                # 409.6 MB of K/V would partly stay in the 256 MB MALL between
+                # iterations: alternate between two copies at different addresses
+                s2 = Staged(call)
+                s2.cache = ba.DeviceCache(s.cache.k.clone(), s.cache.v.clone(),
+                                          call.k_scale, call.v_scale)
+                copies.append(s2)
+            it = {"i": 0}
+
+            def run_attn(copies=copies, it=it):
+                c = copies[it["i"] % len(copies)]
+                it["i"] += 1
+                c.attend("decode")
+            total, per_d = timed_steps([("kvwrite", s.kvwrite), ("decode", run_attn)],
+                                       max(args.steps, 5) * 2, args.warmup)
+            bpk = 2 * HKV * D * (2 if call.kv_dtype == "bf16" else 1)
+            nbytes = visible_keys_decode(ql, kl, kind) * bpk
+            gbs = nbytes / (per_d["decode"] * 1e-3) / 1e9
+            dec[f"config{cfg}-{kind}"] = {
+                "kv_dtype": call.kv_dtype, "seqs": len(ql), "q_len": max(ql),
+                "decode_us": round(per_d["decode"] * 1e3, 2),
+                "kvwrite_us": round(per_d["kvwrite"] * 1e3, 2),
+                "kv_bytes": nbytes, "hbm_gbs": round(gbs, 1),
+                "hbm_frac": round(gbs / PEAK_HBM_GBS, 4),
+                "tokens_per_s": round(sum(ql) / ((per_d["decode"] + per_d["kvwrite"]) * 1e-3), 1),
+            }
+            log(f"  decode config{cfg}-{kind}: {dec[f'config{cfg}-{kind}']}")
+            del s, copies, call
+            torch.cuda.empty_cache()
+    result["decode"] = dec
+
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -174,7 +225,12 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-rows", type=int, default=24, help="oracle rows per layer kind")
+    ap.add_argument("--cpu-rows", type=int, default=96, help="oracle rows per layer kind")
+    ap.add_argument("--only", choices=("all", "prefill", "decode"), default="all",
+                    help="restrict the run (for counter collection); the JSON line needs 'all'")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run one plain 1 GiB device-to-device copy, whose FETCH_SIZE / "
+                         "WRITE_SIZE counters calibrate the traffic of the other kernels")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on exactly one GPU; --gpus {args.gpus} is not supported "
@@ -191,6 +247,20 @@ def main():
     ba.load()
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+
+    if args.copy_calibration:
+        src = torch.ones(1 << 29, dtype=torch.int16, device=dev)     # 1 GiB
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log("copy calibration: 1 GiB device-to-device copy done")
+        del src, dst
+    if args.only == "decode":
+        args.no_cpu_baseline = True
+        result = {"decode": {}}
+        run_decode(args, result)
+        print(json.dumps(result), flush=True)
+        return
 
     # ---------------------------------------------------------------- prefill workload
     log("generating the long-prefill workload (8 x 2048 new on 98304 cached) ...")
@@ -254,46 +324,8 @@ def main():
     del staged, parts
     torch.cuda.empty_cache()
 
-    # ---------------------------------------------------------------- decode workloads
-    if not args.no_decode:
-        dec = {}
-        for cfg in (2, 3, 4):
-            for kind in ("full", "swa"):
-                call = synth.make_config(cfg, kind, cache_device="cuda")
-                s = Staged(call)
-                ql = [int(x) for x in call.q_lens]
-                kl = [int(x) for x in call.kv_len]
-                copies = [s]
-                if cfg == 2 and kind == "full":
-                    # 409.6 MB of K/V would partly stay in the 256 MB MALL between
-                    # iterations: alternate between two copies at different addresses
-                    s2 = Staged(call)
-                    s2.cache = ba.DeviceCache(s.cache.k.clone(), s.cache.v.clone(),
-                                              call.k_scale, call.v_scale)
-                    copies.append(s2)
-                it = {"i": 0}
-
-                def run_attn(copies=copies, it=it):
-                    c = copies[it["i"] % len(copies)]
-                    it["i"] += 1
-                    c.attend("decode")
-                total, per_d = timed_steps([("kvwrite", s.kvwrite), ("decode", run_attn)],
-                                           max(args.steps, 5) * 2, args.warmup)
-                bpk = 2 * HKV * D * (2 if call.kv_dtype == "bf16" else 1)
-                nbytes = visible_keys_decode(ql, kl, kind) * bpk
-                gbs = nbytes / (per_d["decode"] * 1e-3) / 1e9
-                dec[f"config{cfg}-{kind}"] = {
-                    "kv_dtype": call.kv_dtype, "seqs": len(ql), "q_len": max(ql),
-                    "decode_us": round(per_d["decode"] * 1e3, 2),
-                    "kvwrite_us": round(per_d["kvwrite"] * 1e3, 2),
-                    "kv_bytes": nbytes, "hbm_gbs": round(gbs, 1),
-                    "hbm_frac": round(gbs / PEAK_HBM_GBS, 4),
-                    "tokens_per_s": round(sum(ql) / ((per_d["decode"] + per_d["kvwrite"]) * 1e-3), 1),
-                }
-                log(f"  decode config{cfg}-{kind}: {dec[f'config{cfg}-{kind}']}")
-                del s, copies, call
-                torch.cuda.empty_cache()
-        result["decode"] = dec
+    if not args.no_decode and args.only == "all":  # "--only prefill" skips the decode workloads
+        run_decode(args, result)
 
     # ---------------------------------------------------------------- oracle on the host
     if not args.no_cpu_baseline:

@@ -34,21 +34,26 @@
 namespace beam {
 namespace {
 
-// Workgroup shape: RB 32-row MFMA blocks per wave, WAVES waves, 256 rows in all.
+// Workgroup shape: 8 waves (2 per SIMD) x one 32-row MFMA block = 256 rows.
 constexpr int kRowsPerBlock = 256;
-constexpr int kRB = 1;                                   // 32 rows per wave ...
-constexpr int kWaves = kRowsPerBlock / (32 * kRB);       // ... 8 waves, 2 per SIMD
+constexpr int kRowsPerWave = 32;
+constexpr int kWaves = kRowsPerBlock / kRowsPerWave;
 constexpr int kThreads = kWaves * 64;
-constexpr int kRowsPerWave = 32 * kRB;
 constexpr int kRowBytes = kHeadDim * 2;                  // 256-byte bf16 row, swizzled chunks
 constexpr int kTileBytes = kPage * kRowBytes;            // one K or V page tile: 16 KiB
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kRescaleSlack = 8.0f;                    // log2 headroom before rescaling
+constexpr int kNumXcds = 8;                              // MI355X: 8 XCDs x 32 CUs
 
 typedef __attribute__((address_space(3))) void lds_void_t;
 
-// byte offset of 16-byte chunk `c` (0..15) of row `r` inside a swizzled tile
-__device__ __forceinline__ int swz(int r, int c) { return r * kRowBytes + ((c ^ (r & 15)) << 4); }
+// Chunk slot of 16-byte chunk c (0..15) of row r in a swizzled tile: c XOR f(r mod 16),
+// f swapping the two 2-bit halves of r's low nibble. f is a bijection, so the 16 rows a
+// K-operand read touches at one chunk land in 16 distinct slots; and 4 consecutive rows
+// get distinct f(r) >> 2, so the 4 rows x 4 chunks of a transposing V read land in 4
+// distinct 4-slot bank groups.
+__device__ __forceinline__ int swz_key(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
+__device__ __forceinline__ int swz(int r, int c) { return r * kRowBytes + ((c ^ swz_key(r)) << 4); }
 
 __device__ __forceinline__ float swap_halves_max(float x) {
   const uint32_t u = __float_as_uint(x);
@@ -68,9 +73,18 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(
     uint16_t* out, int64_t out_stride) {
   __shared__ __attribute__((aligned(1024))) unsigned char lds[2 * 2 * kTileBytes];
 
-  const int tile = blockIdx.x;
-  const int g = blockIdx.y;
-  const int b = blockIdx.z;
+  // Blocks are dispatched round-robin over the 8 XCDs (each with its own L2). Remap the
+  // linear block id so that each XCD runs a contiguous range of the work list, in which
+  // the row tiles of one (sequence, KV head) are consecutive: the blocks that stream the
+  // same K/V pages then share one L2.
+  const int num_blocks = gridDim.x * gridDim.y * gridDim.z;
+  const int lin = blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z);
+  const int xcd = lin % kNumXcds, slot = lin / kNumXcds;
+  const int per = num_blocks / kNumXcds, extra = num_blocks % kNumXcds;
+  const int work = xcd * per + min(xcd, extra) + slot;
+  const int tile = work % gridDim.x;
+  const int g = (work / gridDim.x) % gridDim.y;
+  const int b = work / (gridDim.x * gridDim.y);
   const int tid = threadIdx.x;
   const int wave = tid / 64;
   const int lane = tid % 64;
@@ -103,216 +117,219 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(
   const int w_max_lo = swa ? max(w_max_pos - L.window + 1, 0) : 0;
   const int w_min_lo = swa ? max(w_min_pos - L.window + 1, 0) : 0;
 
-  // per-lane rows: Q^T operand, position, window start
-  bf16x8_t qop[kRB][8];
-  int row_pos[kRB], row_lo[kRB];
-#pragma unroll
-  for (int rb = 0; rb < kRB; ++rb) {
-    const int r = wrow0 + 32 * rb + lr;
-    const bool valid = wave_active && (r - wrow0) < wrows;
-    const int t = valid ? r / L.G : 0;
-    const int h = g * L.G + (valid ? r % L.G : 0);
-    row_pos[rb] = valid ? first_pos + t : -1;
-    row_lo[rb] = (swa && valid) ? max(row_pos[rb] - L.window + 1, 0) : 0;
+  // per-lane row: Q^T operand, position, window start
+  bf16x8_t qop[8];
+  const int my_row = wrow0 + lr;
+  const bool row_valid = wave_active && lr < wrows;
+  const int row_pos = row_valid ? first_pos + my_row / L.G : -1;
+  const int row_lo = (swa && row_valid) ? max(row_pos - L.window + 1, 0) : 0;
+  {
+    const int t = row_valid ? my_row / L.G : 0;
+    const int h = g * L.G + (row_valid ? my_row % L.G : 0);
     const uint16_t* qrow = q + (int64_t)(q0 + t) * q_stride + (int64_t)h * kHeadDim;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       u32x4_t v = {0u, 0u, 0u, 0u};
-      if (valid) v = *reinterpret_cast<const u32x4_t*>(qrow + 16 * i + 8 * half);
-      qop[rb][i] = __builtin_bit_cast(bf16x8_t, v);
+      if (row_valid) v = *reinterpret_cast<const u32x4_t*>(qrow + 16 * i + 8 * half);
+      qop[i] = __builtin_bit_cast(bf16x8_t, v);
     }
   }
 
   const float c = L.sm_scale * kLog2e;
-  float m_run[kRB], l_run[kRB];
-  f32x16_t acc[kRB][4];
+  float m_run = -INFINITY, l_run = 0.f;
+  f32x16_t acc[4];
 #pragma unroll
-  for (int rb = 0; rb < kRB; ++rb) {
-    m_run[rb] = -INFINITY;
-    l_run[rb] = 0.f;
+  for (int db = 0; db < 4; ++db)
 #pragma unroll
-    for (int db = 0; db < 4; ++db)
+    for (int e = 0; e < 16; ++e) acc[db][e] = 0.f;
+
+  // ---- lane-constant LDS offsets. Every tile row this lane touches has a fixed residue
+  // mod 16, so each swizzled offset is a lane constant plus a compile-time immediate
+  // (buffer, 32-key half, 16-key step).
+  const int grp = lane / 16, gi = lane % 16;
+  int k_off[8];                       // K operand: row lr (+32 per half), chunk 2i + half
 #pragma unroll
-      for (int e = 0; e < 16; ++e) acc[rb][db][e] = 0.f;
+  for (int i = 0; i < 8; ++i) k_off[i] = lr * kRowBytes + (((2 * i + half) ^ swz_key(lr)) << 4);
+  // V operand, transposing reads: rows rv (+8) of each 16-key step, columns
+  // 32*db + 16*(grp%2) + 4*(gi%4) = chunk 4*db + cv, byte 8*(gi%2) inside the chunk
+  const int rv = 4 * (grp / 2) + gi / 4, cv = 2 * (grp % 2) + (gi % 4) / 2;
+  int v_off0[4], v_off1[4];
+#pragma unroll
+  for (int db = 0; db < 4; ++db) {
+    v_off0[db] = rv * kRowBytes + (((4 * db + cv) ^ swz_key(rv)) << 4) + 8 * (gi % 2);
+    v_off1[db] = (rv + 8) * kRowBytes + (((4 * db + cv) ^ swz_key(rv + 8)) << 4) + 8 * (gi % 2);
   }
 
   // ---- direct global -> LDS copy of one K and one V page tile. Wave w copies rows
-  // [w*R, w*R + R) of each (R = 64 / waves): R/4 instructions per tensor, each 64 lanes
-  // x 16 bytes = 4 rows.
-  // Lane l writes LDS bytes [16 l, 16 l + 16) of its 1 KiB block, i.e. row 4i + l/16,
-  // chunk slot l%16, which holds the row's chunk (l%16) ^ (row & 15).
-  const char* kcache = static_cast<const char*>(C.k);
-  const char* vcache = static_cast<const char*>(C.v);
+  // [8w, 8w + 8) of each with 2 instructions per tensor; an instruction moves 64 lanes x
+  // 16 bytes = 4 rows into one contiguous 1 KiB block: lane l lands at row 4i + l/16,
+  // chunk slot l%16, so it fetches that row's chunk (l%16) ^ swz_key(row).
+  constexpr int kRowsCopied = kPage / kWaves;
+  int cp_off[kRowsCopied / 4];
+#pragma unroll
+  for (int i = 0; i < kRowsCopied / 4; ++i) {
+    const int row = kRowsCopied * wave + 4 * i + lane / 16;
+    cp_off[i] = row * kRowBytes + (((lane % 16) ^ swz_key(row)) << 4);
+  }
   const int32_t* bt_row = B.block_table + (int64_t)b * B.max_pages;
-  auto issue_tile = [&](int kt, int buf) {
-    const int64_t page = bt_row[kt];
-    const int64_t base = (page * L.Hkv + g) * (int64_t)kTileBytes;
-    unsigned char* kl = lds + buf * 2 * kTileBytes;
-    unsigned char* vl = kl + kTileBytes;
-    constexpr int kRowsCopied = kPage / kWaves;
+  const int64_t head_off = (int64_t)g * kTileBytes;
+  const int64_t page_bytes = (int64_t)L.Hkv * kTileBytes;
+  auto issue_tile = [&](int kt, auto buf_c) {
+    constexpr int BUF = decltype(buf_c)::value;
+    const int64_t base = (int64_t)bt_row[kt] * page_bytes + head_off;
+    const char* kb = static_cast<const char*>(C.k) + base;
+    const char* vb = static_cast<const char*>(C.v) + base;
 #pragma unroll
     for (int i = 0; i < kRowsCopied / 4; ++i) {
-      const int row = kRowsCopied * wave + 4 * i + lane / 16;
-      const int chunk = (lane % 16) ^ (row & 15);
-      const int64_t src = base + row * kRowBytes + chunk * 16;
-      const int dst = (kRowsCopied * wave + 4 * i) * kRowBytes;  // wave-uniform block start
-      __builtin_amdgcn_global_load_lds(kcache + src, (lds_void_t*)(kl + dst), 16, 0, 0);
-      __builtin_amdgcn_global_load_lds(vcache + src, (lds_void_t*)(vl + dst), 16, 0, 0);
+      const int dst = BUF * 2 * kTileBytes + (kRowsCopied * wave + 4 * i) * kRowBytes;
+      __builtin_amdgcn_global_load_lds(kb + cp_off[i], (lds_void_t*)(lds + dst), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(vb + cp_off[i], (lds_void_t*)(lds + dst + kTileBytes), 16, 0, 0);
     }
   };
 
-  issue_tile(kt_begin, 0);
-  __builtin_amdgcn_s_waitcnt(0);       // vmcnt(0) lgkmcnt(0): this wave's copies landed
-  __syncthreads();
+  // ---- one 64-key tile from LDS buffer BUF: MASK when some key is invisible to some row
+  // of the wave, TAIL when the tile holds slots past the sequence end (NaN allowed there)
+  auto compute = [&](int k0, int buf, auto mask_c, auto tail_c) {
+    constexpr bool MASK = decltype(mask_c)::value;
+    constexpr bool TAIL = decltype(tail_c)::value;
+    // this tile's buffer: rebase the lane offsets once (the halves and 16-key steps are
+    // immediates on top)
+    const int kbase = buf * 2 * kTileBytes;
+    int ka[8], va0[4], va1[4];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) ka[i] = k_off[i] + kbase;
+#pragma unroll
+    for (int db = 0; db < 4; ++db) {
+      va0[db] = v_off0[db] + kbase + kTileBytes;
+      va1[db] = v_off1[db] + kbase + kTileBytes;
+    }
+#pragma unroll
+    for (int kh = 0; kh < 2; ++kh) {         // 32-key halves of the tile
+      __builtin_amdgcn_sched_barrier(0);
+      // ---- S^T = K Q^T for this half
+      bf16x8_t kop[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        kop[i] = *reinterpret_cast<const bf16x8_t*>(lds + kh * 32 * kRowBytes + ka[i]);
+      f32x16_t sc;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) sc[e] = 0.f;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[i], qop[i], sc, 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+      // ---- mask, online softmax, P^T in bf16 (k-slot order of the two 16-key steps)
+      if (MASK) {
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int j = k0 + 32 * kh + (v / 4) * 8 + half * 4 + (v % 4);
+          if (j > row_pos || j < row_lo) sc[v] = -INFINITY;
+        }
+      }
+      float mx = __builtin_fmaxf(__builtin_fmaxf(sc[0], sc[1]), sc[2]);
+#pragma unroll
+      for (int v = 3; v < 16; v += 2) mx = __builtin_fmaxf(__builtin_fmaxf(mx, sc[v]), sc[v + 1 < 16 ? v + 1 : v]);
+      mx = swap_halves_max(mx) * c;
+      // raise the running max only when it grew by more than the slack
+      if (__builtin_amdgcn_ballot_w64(mx > m_run + kRescaleSlack) != 0) {
+        const float m_new = fmaxf(m_run, mx);
+        // 0 when this row saw no key before; 1 when it still sees none
+        const float alpha = m_new == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
+        l_run *= alpha;
+#pragma unroll
+        for (int db = 0; db < 4; ++db) acc[db] *= alpha;
+        m_run = m_new;
+      }
+      const float m_use = m_run == -INFINITY ? 0.f : m_run;
+      bf16x8_t pop[2];
+      float psum = 0.f;
+#pragma unroll
+      for (int cc = 0; cc < 2; ++cc) {
+#pragma unroll
+        for (int jj = 0; jj < 8; ++jj) {
+          const float p = __builtin_amdgcn_exp2f(fmaf(sc[8 * cc + jj], c, -m_use));
+          psum += p;
+          pop[cc][jj] = (__bf16)p;
+        }
+      }
+      l_run += psum;
+      __builtin_amdgcn_sched_barrier(0);
+      // ---- O^T += V^T P^T over the 32 keys of this half (2 MFMA k-steps of 16)
+#pragma unroll
+      for (int cc = 0; cc < 2; ++cc) {
+        const unsigned char* vrow = lds + (32 * kh + 16 * cc) * kRowBytes;
+#pragma unroll
+        for (int db = 0; db < 4; ++db) {
+          i16x4_t t0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (__attribute__((address_space(3))) i16x4_t*)(vrow + va0[db]));
+          i16x4_t t1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (__attribute__((address_space(3))) i16x4_t*)(vrow + va1[db]));
+          if (TAIL) {
+            // this lane received keys kb0 + 0..3 (t0) and kb0 + 8..11 (t1) at one column
+            const int kb0 = k0 + 32 * kh + 16 * cc + 4 * (grp / 2);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              if (kb0 + e >= kv) t0[e] = 0;
+              if (kb0 + 8 + e >= kv) t1[e] = 0;
+            }
+          }
+          const u32x2_t u0 = __builtin_bit_cast(u32x2_t, t0), u1 = __builtin_bit_cast(u32x2_t, t1);
+          const u32x4_t uv = {u0[0], u0[1], u1[0], u1[1]};
+          acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, uv), pop[cc],
+                                                           acc[db], 0, 0, 0);
+        }
+      }
+    }
+  };
 
-  const int grp = lane / 16, gi = lane % 16;
+  issue_tile(kt_begin, std::integral_constant<int, 0>{});
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
   for (int kt = kt_begin; kt < kt_end; ++kt) {
     const int buf = (kt - kt_begin) & 1;
-    if (kt + 1 < kt_end) issue_tile(kt + 1, buf ^ 1);
+    if (kt + 1 < kt_end) {
+      if (buf == 0) issue_tile(kt + 1, std::integral_constant<int, 1>{});
+      else issue_tile(kt + 1, std::integral_constant<int, 0>{});
+    }
     const int k0 = kt * kPage;
     const bool skip = !wave_active || k0 > w_max_pos || k0 + kPage - 1 < w_min_lo;
     if (!skip) {
-      // MASK: some key of the tile is invisible to some row of the wave; TAIL: the tile
-      // holds slots past the sequence end (they may hold NaN; a TAIL tile also masks)
-      auto compute = [&](auto mask_c, auto tail_c) {
-        constexpr bool MASK = decltype(mask_c)::value;
-        constexpr bool TAIL = decltype(tail_c)::value;
-        const unsigned char* kt_lds = lds + buf * 2 * kTileBytes;
-        const unsigned char* vt_lds = kt_lds + kTileBytes;
-  #pragma unroll 1
-        for (int kh = 0; kh < 2; ++kh) {         // 32-key halves of the tile
-          // ---- S^T = K Q^T for this half, two row blocks
-          f32x16_t sc[kRB];
-  #pragma unroll
-          for (int rb = 0; rb < kRB; ++rb)
-  #pragma unroll
-            for (int e = 0; e < 16; ++e) sc[rb][e] = 0.f;
-          const int krow = 32 * kh + lr;
-          __builtin_amdgcn_sched_barrier(0);
-          bf16x8_t kop[8];
-  #pragma unroll
-          for (int i = 0; i < 8; ++i)
-            kop[i] = *reinterpret_cast<const bf16x8_t*>(kt_lds + swz(krow, 2 * i + half));
-  #pragma unroll
-          for (int i = 0; i < 8; ++i)
-  #pragma unroll
-            for (int rb = 0; rb < kRB; ++rb)
-              sc[rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[i], qop[rb][i], sc[rb], 0, 0, 0);
-          __builtin_amdgcn_sched_barrier(0);
-          // ---- mask, online softmax, P^T in bf16
-          bf16x8_t pop[kRB][2];
-  #pragma unroll
-          for (int rb = 0; rb < kRB; ++rb) {
-            if (MASK) {
-  #pragma unroll
-              for (int v = 0; v < 16; ++v) {
-                const int j = k0 + 32 * kh + (v / 4) * 8 + half * 4 + (v % 4);
-                if (j > row_pos[rb] || j < row_lo[rb]) sc[rb][v] = -INFINITY;
-              }
-            }
-            float mx = fmaxf(sc[rb][0], sc[rb][1]);
-  #pragma unroll
-            for (int v = 2; v < 16; ++v) mx = fmaxf(mx, sc[rb][v]);
-            mx = swap_halves_max(mx) * c;
-            // raise the running max only when it grew by more than the slack
-            if (__builtin_amdgcn_ballot_w64(mx > m_run[rb] + kRescaleSlack) != 0) {
-              const float m_new = fmaxf(m_run[rb], mx);
-              // 0 when this row saw no key before; 1 when it still sees none
-              const float alpha = m_new == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m_run[rb] - m_new);
-              l_run[rb] *= alpha;
-  #pragma unroll
-              for (int db = 0; db < 4; ++db) acc[rb][db] *= alpha;
-              m_run[rb] = m_new;
-            }
-            const float m_use = m_run[rb] == -INFINITY ? 0.f : m_run[rb];
-            float psum = 0.f;
-  #pragma unroll
-            for (int cc = 0; cc < 2; ++cc) {
-              bf16x8_t pb;
-  #pragma unroll
-              for (int jj = 0; jj < 8; ++jj) {
-                const float p = __builtin_amdgcn_exp2f(fmaf(sc[rb][8 * cc + jj], c, -m_use));
-                psum += p;
-                pb[jj] = (__bf16)p;
-              }
-              pop[rb][cc] = pb;
-            }
-            l_run[rb] += psum;
-          }
-          __builtin_amdgcn_sched_barrier(0);
-          // ---- O^T += V^T P^T over the 32 keys of this half (2 MFMA k-steps of 16)
-  #pragma unroll
-          for (int cc = 0; cc < 2; ++cc) {
-            const int key0 = 32 * kh + 16 * cc + 4 * (grp / 2) + gi / 4;   // row read by this lane
-  #pragma unroll
-            for (int db = 0; db < 4; ++db) {
-              const int col = 32 * db + 16 * (grp % 2) + 4 * (gi % 4);    // bf16 element column
-              const int off0 = swz(key0, col / 8) + (col % 8) * 2;
-              const int off1 = swz(key0 + 8, col / 8) + (col % 8) * 2;
-              i16x4_t t0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                  (__attribute__((address_space(3))) i16x4_t*)(vt_lds + off0));
-              i16x4_t t1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                  (__attribute__((address_space(3))) i16x4_t*)(vt_lds + off1));
-              if (TAIL) {
-                // this lane received keys key0-(gi/4)+0..3 (t0) and +8 (t1) at one column
-                const int kb0 = k0 + 32 * kh + 16 * cc + 4 * (grp / 2);
-  #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                  if (kb0 + e >= kv) t0[e] = 0;
-                  if (kb0 + 8 + e >= kv) t1[e] = 0;
-                }
-              }
-              const u32x2_t u0 = __builtin_bit_cast(u32x2_t, t0), u1 = __builtin_bit_cast(u32x2_t, t1);
-              const u32x4_t uv = {u0[0], u0[1], u1[0], u1[1]};
-              const bf16x8_t vop = __builtin_bit_cast(bf16x8_t, uv);
-  #pragma unroll
-              for (int rb = 0; rb < kRB; ++rb)
-                acc[rb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop, pop[rb][cc], acc[rb][db], 0, 0, 0);
-            }
-          }
-        }
-      };
       const bool need_mask = (k0 + kPage - 1 > w_min_pos) || (k0 < w_max_lo);
-      if (k0 + kPage > kv) compute(std::true_type{}, std::true_type{});
-      else if (need_mask) compute(std::true_type{}, std::false_type{});
-      else compute(std::false_type{}, std::false_type{});
+      if (k0 + kPage > kv) compute(k0, buf, std::true_type{}, std::true_type{});
+      else if (need_mask) compute(k0, buf, std::true_type{}, std::false_type{});
+      else compute(k0, buf, std::false_type{}, std::false_type{});
     }
     __builtin_amdgcn_s_waitcnt(0);     // this wave's copies of the next tile landed
-    __syncthreads();                   // ... and everyone's; the current buffer is free
+    __syncthreads();                   // ... and everyone's; this buffer is free again
   }
 
-  // ---- epilogue: 1/l, gate, bf16 store (lane owns row lr of each block; d values
+  // ---- epilogue: 1/l, gate, bf16 store (lane owns row lr; d values
   // 32*db + 8*(v/4) + 4*half + (v%4))
+  const float lsum = swap_halves_sum(l_run);
+  if (!row_valid) return;
+  const int t = my_row / L.G;
+  const int h = g * L.G + my_row % L.G;
+  const int64_t tok = q0 + t;
+  const float inv = lsum > 0.f ? 1.0f / lsum : 0.f;
+  const float bh = gate != nullptr ? bf16_to_f32(gate_bias[h]) : 0.f;
 #pragma unroll
-  for (int rb = 0; rb < kRB; ++rb) {
-    const float lsum = swap_halves_sum(l_run[rb]);
-    const int r = wrow0 + 32 * rb + lr;
-    if (!wave_active || (r - wrow0) >= wrows) continue;
-    const int t = r / L.G;
-    const int h = g * L.G + r % L.G;
-    const int64_t tok = q0 + t;
-    const float inv = lsum > 0.f ? 1.0f / lsum : 0.f;
-    const float bh = gate != nullptr ? bf16_to_f32(gate_bias[h]) : 0.f;
+  for (int db = 0; db < 4; ++db)
 #pragma unroll
-    for (int db = 0; db < 4; ++db)
+    for (int q4 = 0; q4 < 4; ++q4) {
+      const int d = 32 * db + 8 * q4 + 4 * half;
+      float y[4];
 #pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        const int d = 32 * db + 8 * q4 + 4 * half;
-        float y[4];
+      for (int e = 0; e < 4; ++e) y[e] = acc[db][4 * q4 + e] * inv;
+      if (gate != nullptr) {
+        const u32x2_t gw = *reinterpret_cast<const u32x2_t*>(gate + tok * gate_stride + (int64_t)h * kHeadDim + d);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) y[e] = acc[rb][db][4 * q4 + e] * inv;
-        if (gate != nullptr) {
-          const u32x2_t gw = *reinterpret_cast<const u32x2_t*>(gate + tok * gate_stride + (int64_t)h * kHeadDim + d);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const float gv = bf16_to_f32((gw[e / 2] >> (16 * (e % 2))) & 0xFFFFu) + bh;
-            y[e] *= 1.0f / (1.0f + expf(-gv));
-          }
+        for (int e = 0; e < 4; ++e) {
+          const float gv = bf16_to_f32((gw[e / 2] >> (16 * (e % 2))) & 0xFFFFu) + bh;
+          y[e] *= 1.0f / (1.0f + expf(-gv));
         }
-        const u32x2_t o = {pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3])};
-        *reinterpret_cast<u32x2_t*>(out + tok * out_stride + (int64_t)h * kHeadDim + d) = o;
       }
-  }
+      const u32x2_t o = {pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3])};
+      *reinterpret_cast<u32x2_t*>(out + tok * out_stride + (int64_t)h * kHeadDim + d) = o;
+    }
 }
 
 }  // namespace
