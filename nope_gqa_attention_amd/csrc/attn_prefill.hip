@@ -11,23 +11,30 @@
 //  * Rows are (token, query head) pairs of one KV head's group, flattened token-major:
 //    a workgroup owns 256 consecutive rows (about 43 tokens x 6 heads), so every K/V
 //    tile it stages in LDS serves all 6 query heads of the group (GQA reuse) and all of
-//    its tokens. Grid: (row tile, KV head, sequence).
+//    its tokens. Grid: (row tile, KV head, sequence), remapped so that the row tiles of
+//    one (sequence, KV head) run on one XCD and share its L2.
 //  * K/V tiles are one 64-token page of one KV head (16 KiB each), copied straight from
 //    global memory into LDS with gfx950's global_load_lds_dwordx4 (no staging registers)
 //    and double-buffered: the next page is in flight while the current one is consumed.
 //    Each 256-byte row is stored with its 16-byte chunks XOR-swizzled by the row index so
-//    that the operand reads below hit distinct LDS banks.
-//  * 4 waves x 64 rows. Per 32-key half of a tile a wave computes S^T = K Q^T with MFMA
-//    32x32x16 bf16 for two 32-row blocks sharing each K operand; a lane then holds 16
-//    scores of one row, so row max/sum take one cross-half swap (permlane32).
+//    that the operand reads below hit distinct LDS banks. The block table is read 64
+//    entries at a time, one chunk ahead.
+//  * 8 waves (2 per SIMD) x 32 rows. Per 32-key half of a tile a wave computes
+//    S^T = K Q^T with MFMA 32x32x16 bf16 (K from LDS, Q^T held in registers); a lane
+//    then holds 16 scores of one row, so row max/sum take one cross-half swap
+//    (permlane32).
 //  * O^T += V^T P^T: P^T is the score accumulator packed to bf16 in place (its key order
 //    is the MFMA's k-slot order); V^T comes from the row-major V tile through the
-//    transposing LDS read ds_read_b64_tr_b16.
+//    transposing LDS read ds_read_b64_tr_b16. The V reads and the next half's K reads
+//    are issued before the softmax so that their latency hides behind it.
 //  * The running maximum is only raised when a row's maximum grows by more than 2^8
 //    (log2 domain), so the 128-value output rescale is skipped on almost every tile;
 //    the final division by the same running sum keeps the result exact.
-//  * Fully visible tiles skip the mask; tiles wholly outside a wave's rows skip compute.
+//  * Tiles that every row of the workgroup sees whole run in a loop of their own with no
+//    mask; the masked tiles at the window start and at the diagonal run in separate
+//    loops, where tiles wholly outside a wave's rows skip compute.
 #include <type_traits>
+#include <utility>
 
 #include "beam_common.h"
 
@@ -59,6 +66,33 @@ __device__ __forceinline__ float swap_halves_max(float x) {
   const uint32_t u = __float_as_uint(x);
   const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
   return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+template <typename F, int... I>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+// f(integral_constant<int, i>) for i = 0 .. N-1, so that i can feed immediates
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
+// Transposing 8-byte LDS read (ds_read_b64_tr_b16) at a 32-bit LDS byte address + OFF.
+template <int OFF>
+__device__ __forceinline__ u32x2_t lds_read_tr(uint32_t addr) {
+  u32x2_t r;
+  asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "i"(OFF));
+  return r;
+}
+// Wait for every outstanding LDS read; the values are threaded through the wait so that
+// no use of them is scheduled before it.
+__device__ __forceinline__ void lds_wait_all(u32x2_t (&v)[2][4][2]) {
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+  for (int a = 0; a < 2; ++a)
+#pragma unroll
+    for (int b = 0; b < 4; ++b)
+#pragma unroll
+      for (int c = 0; c < 2; ++c) asm volatile("" : "+v"(v[a][b][c]));
 }
 __device__ __forceinline__ float swap_halves_sum(float x) {
   const uint32_t u = __float_as_uint(x);
@@ -147,6 +181,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(
   // mod 16, so each swizzled offset is a lane constant plus a compile-time immediate
   // (buffer, 32-key half, 16-key step).
   const int grp = lane / 16, gi = lane % 16;
+  const uint32_t lds_addr = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) unsigned char*)lds;
   int k_off[8];                       // K operand: row lr (+32 per half), chunk 2i + half
 #pragma unroll
   for (int i = 0; i < 8; ++i) k_off[i] = lr * kRowBytes + (((2 * i + half) ^ swz_key(lr)) << 4);
@@ -172,11 +207,26 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(
     cp_off[i] = row * kRowBytes + (((lane % 16) ^ swz_key(row)) << 4);
   }
   const int32_t* bt_row = B.block_table + (int64_t)b * B.max_pages;
+  // Physical pages of the tiles, 64 per chunk, one entry per lane: chunk c holds tiles
+  // kt_begin + 64c + lane. The next chunk is loaded while the current one is in use, so
+  // the per-tile lookup is a register read, not a memory round trip.
+  auto load_chunk = [&](int c) {
+    const int t = kt_begin + 64 * c + lane;
+    return t < kt_end ? bt_row[t] : 0;
+  };
+  int bt_cur = load_chunk(0);
+  int bt_next = load_chunk(1);
   const int64_t head_off = (int64_t)g * kTileBytes;
   const int64_t page_bytes = (int64_t)L.Hkv * kTileBytes;
   auto issue_tile = [&](int kt, auto buf_c) {
     constexpr int BUF = decltype(buf_c)::value;
-    const int64_t base = (int64_t)bt_row[kt] * page_bytes + head_off;
+    const int rel = kt - kt_begin;
+    if ((rel & 63) == 0 && rel > 0) {
+      bt_cur = bt_next;
+      bt_next = load_chunk(rel / 64 + 1);
+    }
+    const int page = __builtin_amdgcn_readlane(bt_cur, rel & 63);
+    const int64_t base = (int64_t)page * page_bytes + head_off;
     const char* kb = static_cast<const char*>(C.k) + base;
     const char* vb = static_cast<const char*>(C.v) + base;
 #pragma unroll
@@ -192,30 +242,45 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(
   auto compute = [&](int k0, int buf, auto mask_c, auto tail_c) {
     constexpr bool MASK = decltype(mask_c)::value;
     constexpr bool TAIL = decltype(tail_c)::value;
-    // this tile's buffer: rebase the lane offsets once (the halves and 16-key steps are
-    // immediates on top)
-    const int kbase = buf * 2 * kTileBytes;
-    int ka[8], va0[4], va1[4];
+    const unsigned char* tl = lds + buf * 2 * kTileBytes;      // this tile's K; V follows
+    // per-lane LDS byte addresses of this tile's V operand rows (halves and 16-key steps
+    // are immediate offsets on top)
+    const uint32_t vbase = lds_addr + buf * 2 * kTileBytes + kTileBytes;
+    uint32_t va0[4], va1[4];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) ka[i] = k_off[i] + kbase;
+    for (int db = 0; db < 4; ++db) { va0[db] = vbase + v_off0[db]; va1[db] = vbase + v_off1[db]; }
+    // K operands of the first half; the second half's are read while the first computes
+    bf16x8_t kop[8];
 #pragma unroll
-    for (int db = 0; db < 4; ++db) {
-      va0[db] = v_off0[db] + kbase + kTileBytes;
-      va1[db] = v_off1[db] + kbase + kTileBytes;
-    }
-#pragma unroll
-    for (int kh = 0; kh < 2; ++kh) {         // 32-key halves of the tile
+    for (int i = 0; i < 8; ++i) kop[i] = *reinterpret_cast<const bf16x8_t*>(tl + k_off[i]);
+    static_for<2>([&](auto kh_c) {           // 32-key halves of the tile
+      constexpr int kh = decltype(kh_c)::value;
       __builtin_amdgcn_sched_barrier(0);
       // ---- S^T = K Q^T for this half
-      bf16x8_t kop[8];
-#pragma unroll
-      for (int i = 0; i < 8; ++i)
-        kop[i] = *reinterpret_cast<const bf16x8_t*>(lds + kh * 32 * kRowBytes + ka[i]);
       f32x16_t sc;
 #pragma unroll
       for (int e = 0; e < 16; ++e) sc[e] = 0.f;
+      __builtin_amdgcn_s_setprio(1);
 #pragma unroll
       for (int i = 0; i < 8; ++i) sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[i], qop[i], sc, 0, 0, 0);
+      __builtin_amdgcn_s_setprio(0);
+      // V^T operands of this half (transposing reads, inline assembly: the tile has landed,
+      // and the compiler would otherwise also wait for the next tile's copy in flight)
+      u32x2_t vr[2][4][2];
+      static_for<2>([&](auto cc_c) {
+        constexpr int cc = decltype(cc_c)::value;
+        constexpr int off = (32 * kh + 16 * cc) * kRowBytes;
+#pragma unroll
+        for (int db = 0; db < 4; ++db) {
+          vr[cc][db][0] = lds_read_tr<off>(va0[db]);
+          vr[cc][db][1] = lds_read_tr<off>(va1[db]);
+        }
+      });
+      if (kh == 0) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+          kop[i] = *reinterpret_cast<const bf16x8_t*>(tl + 32 * kRowBytes + k_off[i]);
+      }
       __builtin_amdgcn_sched_barrier(0);
       // ---- mask, online softmax, P^T in bf16 (k-slot order of the two 16-key steps)
       if (MASK) {
@@ -252,55 +317,70 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(
         }
       }
       l_run += psum;
+      lds_wait_all(vr);
       __builtin_amdgcn_sched_barrier(0);
       // ---- O^T += V^T P^T over the 32 keys of this half (2 MFMA k-steps of 16)
+      __builtin_amdgcn_s_setprio(1);
 #pragma unroll
-      for (int cc = 0; cc < 2; ++cc) {
-        const unsigned char* vrow = lds + (32 * kh + 16 * cc) * kRowBytes;
+      for (int cc = 0; cc < 2; ++cc)
 #pragma unroll
         for (int db = 0; db < 4; ++db) {
-          i16x4_t t0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (__attribute__((address_space(3))) i16x4_t*)(vrow + va0[db]));
-          i16x4_t t1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (__attribute__((address_space(3))) i16x4_t*)(vrow + va1[db]));
+          u32x2_t u0 = vr[cc][db][0], u1 = vr[cc][db][1];
           if (TAIL) {
-            // this lane received keys kb0 + 0..3 (t0) and kb0 + 8..11 (t1) at one column
+            // this lane received keys kb0 + 0..3 (u0) and kb0 + 8..11 (u1) at one column
             const int kb0 = k0 + 32 * kh + 16 * cc + 4 * (grp / 2);
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-              if (kb0 + e >= kv) t0[e] = 0;
-              if (kb0 + 8 + e >= kv) t1[e] = 0;
+              const uint32_t m = 0xFFFFu << (16 * (e % 2));
+              if (kb0 + e >= kv) u0[e / 2] &= ~m;
+              if (kb0 + 8 + e >= kv) u1[e / 2] &= ~m;
             }
           }
-          const u32x2_t u0 = __builtin_bit_cast(u32x2_t, t0), u1 = __builtin_bit_cast(u32x2_t, t1);
           const u32x4_t uv = {u0[0], u0[1], u1[0], u1[1]};
           acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, uv), pop[cc],
                                                            acc[db], 0, 0, 0);
         }
-      }
+      __builtin_amdgcn_s_setprio(0);
+    });
+  };
+
+  // Tiles every row of the workgroup sees whole need no mask; they form one contiguous
+  // range [plain_begin, plain_end). The masked tiles before it (window start) and after
+  // it (diagonal, sequence end) run a separate loop, so that each loop body has a single
+  // straight-line compute and the accumulators stay in place across iterations.
+  const int blk_max_lo = swa ? max(pos_last - L.window + 1, 0) : 0;
+  const int plain_begin = min(max((blk_max_lo + kPage - 1) / kPage, kt_begin), kt_end);
+  const int plain_end = max(min((pos_first + 1) / kPage, kt_end), plain_begin);
+  int buf = 0;
+  auto advance = [&](int kt) {
+    if (kt + 1 < kt_end) {
+      if (buf == 0) issue_tile(kt + 1, std::integral_constant<int, 1>{});
+      else issue_tile(kt + 1, std::integral_constant<int, 0>{});
     }
+  };
+  auto finish = [&]() {
+    __builtin_amdgcn_s_waitcnt(0);     // this wave's copies of the next tile landed
+    __syncthreads();                   // ... and everyone's; this buffer is free again
+    buf ^= 1;
+  };
+  auto masked_step = [&](int kt) {
+    advance(kt);
+    const int k0 = kt * kPage;
+    const bool skip = !wave_active || k0 > w_max_pos || k0 + kPage - 1 < w_min_lo;
+    if (!skip) compute(k0, buf, std::true_type{}, std::true_type{});
+    finish();
   };
 
   issue_tile(kt_begin, std::integral_constant<int, 0>{});
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-  for (int kt = kt_begin; kt < kt_end; ++kt) {
-    const int buf = (kt - kt_begin) & 1;
-    if (kt + 1 < kt_end) {
-      if (buf == 0) issue_tile(kt + 1, std::integral_constant<int, 1>{});
-      else issue_tile(kt + 1, std::integral_constant<int, 0>{});
-    }
-    const int k0 = kt * kPage;
-    const bool skip = !wave_active || k0 > w_max_pos || k0 + kPage - 1 < w_min_lo;
-    if (!skip) {
-      const bool need_mask = (k0 + kPage - 1 > w_min_pos) || (k0 < w_max_lo);
-      if (k0 + kPage > kv) compute(k0, buf, std::true_type{}, std::true_type{});
-      else if (need_mask) compute(k0, buf, std::true_type{}, std::false_type{});
-      else compute(k0, buf, std::false_type{}, std::false_type{});
-    }
-    __builtin_amdgcn_s_waitcnt(0);     // this wave's copies of the next tile landed
-    __syncthreads();                   // ... and everyone's; this buffer is free again
+  for (int kt = kt_begin; kt < plain_begin; ++kt) masked_step(kt);
+  for (int kt = plain_begin; kt < plain_end; ++kt) {
+    advance(kt);
+    compute(kt * kPage, buf, std::false_type{}, std::false_type{});
+    finish();
   }
+  for (int kt = plain_end; kt < kt_end; ++kt) masked_step(kt);
 
   // ---- epilogue: 1/l, gate, bf16 store (lane owns row lr; d values
   // 32*db + 8*(v/4) + 4*half + (v%4))
