@@ -30,10 +30,83 @@ sys.path.insert(0, ROOT)
 HQ, HKV, D = 48, 8, 128
 PEAK_BF16_TFLOPS = 2500.0        # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0            # MI355X HBM3E
+PREFILL_SRC = os.path.join(ROOT, "nope_gqa_attention_amd", "csrc", "attn_prefill.hip")
+TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "prefill_full_8x2048_on_98304_hbm_traffic.md")
+CALIBRATION_BYTES = 1 << 30      # the plain device-to-device copy run by --copy-calibration
 
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
+
+
+def file_sha256(path):
+    import hashlib
+
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def summarize_counters(paths):
+    """Markdown summary of rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE counter CSVs of a bench
+    run with --copy-calibration: per libbeamattn kernel, the mean KiB per dispatch of each
+    counter and the HBM bytes they stand for once scaled by what the same counter read for
+    the plain 1 GiB copy. Ends with the record the bench line's roofline.traffic is read
+    from, tagged with the hash of the prefill kernel source it was measured on."""
+    import collections
+    import csv
+    import re
+
+    per = collections.defaultdict(lambda: collections.defaultdict(list))
+    calib = {}
+    for path in paths:
+        for r in csv.DictReader(open(path)):
+            name, ctr, val = r["Kernel_Name"], r["Counter_Name"], float(r["Counter_Value"])
+            if "copyBuffer" in name:
+                calib[ctr] = max(calib.get(ctr, 0.0), val)
+            elif "beam::" in name:
+                short = re.sub(r"\(.*", "", name.replace("(anonymous namespace)::", ""))
+                short = short.replace("void ", "")
+                per[short][ctr].append(val)
+    factor = {c: CALIBRATION_BYTES / 1024 / v for c, v in calib.items() if v > 0}
+    lines = ["| kernel | dispatches | FETCH_SIZE KiB | WRITE_SIZE KiB | HBM GB per dispatch |",
+             "|---|---|---|---|---|"]
+    record = None
+    for k in sorted(per):
+        f = per[k].get("FETCH_SIZE", [])
+        w = per[k].get("WRITE_SIZE", [])
+        fm = sum(f) / len(f) if f else None
+        wm = sum(w) / len(w) if w else None
+        gb = None
+        if fm is not None and wm is not None and factor.get("FETCH_SIZE") and factor.get("WRITE_SIZE"):
+            gb = (fm * factor["FETCH_SIZE"] + wm * factor["WRITE_SIZE"]) * 1024 / 1e9
+        lines.append(f"| {k} | {max(len(f), len(w))} | {fm if fm is None else round(fm, 1)} | "
+                     f"{wm if wm is None else round(wm, 1)} | {gb if gb is None else round(gb, 3)} |")
+        if k.endswith("prefill_kernel<1>") and gb is not None:
+            record = round(gb * 1e9)
+    lines.append("")
+    lines.append(f"calibration (1 GiB copy): FETCH_SIZE {calib.get('FETCH_SIZE')} KiB -> factor "
+                 f"{round(factor.get('FETCH_SIZE', 0), 4)}; WRITE_SIZE {calib.get('WRITE_SIZE')} KiB "
+                 f"-> factor {round(factor.get('WRITE_SIZE', 0), 4)}")
+    if record is not None:
+        lines.append(f"traffic-record: kernel=prefill_kernel<1> bytes_per_launch={record} "
+                     f"source_sha256={file_sha256(PREFILL_SRC)}")
+    return "\n".join(lines)
+
+
+def recorded_traffic():
+    """HBM bytes per launch of the full-layer prefill kernel from the committed counter
+    summary, or None when that summary is missing or was taken on another version of the
+    kernel source."""
+    try:
+        text = open(TRAFFIC_SUMMARY).read()
+    except OSError:
+        return None
+    for line in text.splitlines():
+        if line.startswith("traffic-record:"):
+            kv = dict(tok.split("=", 1) for tok in line.split()[1:] if "=" in tok)
+            if kv.get("source_sha256") == file_sha256(PREFILL_SRC):
+                return int(kv["bytes_per_launch"])
+    return None
 
 
 def visible_pairs(q_lens, kv_lens, kind, window=512):
@@ -225,13 +298,19 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-rows", type=int, default=96, help="oracle rows per layer kind")
+    ap.add_argument("--cpu-rows", type=int, default=200, help="oracle rows per layer kind")
     ap.add_argument("--only", choices=("all", "prefill", "decode"), default="all",
                     help="restrict the run (for counter collection); the JSON line needs 'all'")
+    ap.add_argument("--summarize-counters", nargs="+", metavar="CSV",
+                    help="print the markdown summary of rocprofv3 FETCH_SIZE / WRITE_SIZE counter "
+                         "CSVs (no GPU work)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one plain 1 GiB device-to-device copy, whose FETCH_SIZE / "
                          "WRITE_SIZE counters calibrate the traffic of the other kernels")
     args = ap.parse_args()
+    if args.summarize_counters:
+        print(summarize_counters(args.summarize_counters))
+        return
     if args.gpus != 1:
         print(f"bench.py runs on exactly one GPU; --gpus {args.gpus} is not supported "
               "(this build has no multi-GPU path)", file=sys.stderr)
@@ -309,7 +388,8 @@ def main():
                    "global_batch": 8, "seq_len": 2048, "cached_tokens": 98304,
                    "parallelism": "none (1 GPU)"},
         "roofline": {"bound": "mfma", "achieved": dom["prefill_tflops"], "peak": PEAK_BF16_TFLOPS,
-                     "unit": "TFLOP/s", "frac": dom["prefill_mfma_frac"], "traffic": None,
+                     "unit": "TFLOP/s", "frac": dom["prefill_mfma_frac"],
+                     "traffic": recorded_traffic(),
                      "kernel": "prefill_kernel (full NoPE layer)",
                      "algorithmic_flop_per_launch": flops["full"]},
         "layers": layers,
