@@ -31,11 +31,26 @@ beam_status ok() {
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 // Decode work split: a workgroup (4 waves, one page per wave per step) covers
-// keys_per_split keys of one (sequence, KV head, row chunk). The split count aims at
-// about kDecodeTargetWorkgroups workgroups for a batch of max-length sequences. A split
-// is at least as long as keeps its partial results (rows x 130 fp32 written, then read
-// by the merge) near 1.5% of the fp8 K/V bytes it reads (256 bytes per key).
-constexpr int64_t kDecodeTargetWorkgroups = 2048;
+// keys_per_split keys of one (sequence, KV head, row chunk). A split is at least as
+// long as keeps its partial results (rows x 130 fp32 written, then read by the merge)
+// near 1.5% of the fp8 K/V bytes it reads (256 bytes per key). The count of splits is
+// set against the workgroups the device holds at once (CUs x resident workgroups per
+// CU, "slots"):
+//  * one sequence: every split has the same length, so pick the length that minimizes
+//    (rounds of slots) x (keys per split + a fixed cost of about 128 keys per
+//    workgroup) -- a few more workgroups than slots would otherwise run a second, almost
+//    empty round;
+//  * several sequences: their lengths are only known on the device, so aim at about 32
+//    workgroups per CU sized for the longest (measured best on a 32-sequence batch of
+//    8K..128K keys); workgroups past a shorter sequence's end exit at once and the
+//    dispatcher balances the rest.
+int decode_cu_count() {
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
+    cus = 256;
+  return cus;
+}
 
 beam::DecodeSplit choose_decode_split(int32_t G, int32_t kind, int32_t window, int32_t num_seqs,
                                       int32_t max_q_len, int64_t max_kv_len, int32_t Hkv) {
@@ -52,15 +67,29 @@ beam::DecodeSplit choose_decode_split(int32_t G, int32_t kind, int32_t window, i
     if (w < range) range = w;
   }
   if (range < 1) range = 1;
-  const int64_t unit = (int64_t)num_seqs * Hkv * s.row_chunks;
-  int64_t want = unit > 0 ? (kDecodeTargetWorkgroups + unit - 1) / unit : 1;
-  if (want < 1) want = 1;
+  const int64_t unit = (int64_t)num_seqs * Hkv * s.row_chunks;   // workgroups per split index
+  const int64_t slots = (int64_t)decode_cu_count() * beam::decode_wgs_per_cu(s.rows_per_chunk / 16);
   const int64_t step = beam::kDecodeKeysPerBlockStep;
   const int64_t rows_in_chunk = rows < s.rows_per_chunk ? rows : s.rows_per_chunk;
-  const int64_t min_keys = rows_in_chunk * (beam::kHeadDim + 2) * 4 * 64 / 256;
-  int64_t kps = (range + want - 1) / want;
-  if (kps < min_keys) kps = min_keys;
-  kps = ((kps + step - 1) / step) * step;
+  int64_t min_keys = rows_in_chunk * (beam::kHeadDim + 2) * 4 * 64 / 256;
+  min_keys = ((min_keys + step - 1) / step) * step;
+  const int64_t max_keys = ((range + step - 1) / step) * step;
+  if (min_keys > max_keys) min_keys = max_keys;
+  int64_t kps = min_keys;
+  if (num_seqs == 1) {
+    double best = -1.0;
+    for (int64_t k = min_keys; k <= max_keys; k += step) {
+      const int64_t wgs = unit * ((range + k - 1) / k);
+      const double cost = (double)((wgs + slots - 1) / slots) * (double)(k + 128);
+      if (best < 0.0 || cost < best) { best = cost; kps = k; }
+    }
+  } else {
+    const int64_t target = 32 * (int64_t)decode_cu_count();
+    const int64_t want = (target + unit - 1) / unit;                 // splits per sequence
+    kps = (range + want - 1) / want;
+    kps = ((kps + step - 1) / step) * step;
+    if (kps < min_keys) kps = min_keys;
+  }
   s.keys_per_split = (int32_t)kps;
   s.num_splits = (int32_t)((range + kps - 1) / kps);
   if (s.num_splits < 1) s.num_splits = 1;

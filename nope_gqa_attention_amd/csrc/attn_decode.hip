@@ -22,6 +22,8 @@
 //  * P V uses O^T = V^T P^T: P^T is the score accumulator re-packed to bf16 in place;
 //    V^T comes from a row-major LDS copy of the V rows through the gfx950 transposing
 //    LDS read (ds_read_b64_tr_b16), so no register transpose is needed.
+//  * The running max is raised only when a row's maximum grows by more than 2^8 (log2
+//    domain), so the output rescale is skipped on almost every step.
 //  * The 4 waves merge their (max, sum, output) in LDS; splits are merged by
 //    log-sum-exp in a second kernel, which also applies the gate; with one split the
 //    first kernel writes the gated output itself.
@@ -35,6 +37,7 @@ constexpr int kVRowBytes = kHeadDim * 2 + 16;     // bf16 V row in LDS, padded
 constexpr int kVRowsPerWave = 32;                 // keys staged per half-page step
 constexpr int kLdsBytes = kDecodeWaves * kVRowsPerWave * kVRowBytes;
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kRescaleSlack = 8.0f;                // log2 headroom before rescaling
 
 // Start of the 8-value slice of head dimension used by MFMA i (0..3) in lane group g
 // (lane / 16). bf16: one 16-byte load per MFMA; fp8: one 16-byte load feeds 2 MFMAs.
@@ -72,7 +75,7 @@ __device__ __forceinline__ int64_t range_base(const LayerParams& L, int64_t kv, 
 }
 
 template <int KV, int RB>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(RB == 1 ? 2 : 1))) void decode_split_kernel(
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(decode_wgs_per_cu(RB)))) void decode_split_kernel(
     LayerParams L, BatchParams B, CacheParams C, DecodeSplit S,
     const uint16_t* __restrict__ q, int64_t q_stride, const uint16_t* __restrict__ gate,
     int64_t gate_stride, const uint16_t* __restrict__ gate_bias, uint16_t* out,
@@ -105,14 +108,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(RB == 
 
   // ---- this lane's rows: Q^T operand, position and window start
   bf16x8_t qop[RB][4];
-  int64_t row_pos[RB], row_lo[RB];
+  int row_pos[RB], row_lo[RB];        // positions fit in 32 bits (kv_len is int32)
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) {
     const int64_t r = row0 + 16 * rb + lc;
     const bool valid = r < rows_b && (r - row0) < S.rows_per_chunk;
     const int64_t t = valid ? r / L.G : 0;
     const int h = g * L.G + (int)(valid ? r % L.G : 0);
-    row_pos[rb] = valid ? first_pos + t : -1;
+    row_pos[rb] = valid ? (int)(first_pos + t) : -1;
     row_lo[rb] = (L.kind == BEAM_LAYER_SWA && valid)
                      ? (row_pos[rb] - L.window + 1 > 0 ? row_pos[rb] - L.window + 1 : 0) : 0;
     const uint16_t* qrow = q + (q0 + t) * q_stride + (int64_t)h * kHeadDim;
@@ -140,11 +143,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(RB == 
   }
 
   unsigned char* vlds = lds + wave * kVRowsPerWave * kVRowBytes;
-  const int64_t head_elems = (int64_t)kPage * kHeadDim;   // one KV head's page
 
   // This wave's pages: keys pk = k_begin + 64*(wave + 4*pi), pi = 0, 1, ...; each page is
-  // two half-steps of 32 keys. Half-step j+1 is fetched into registers while half-step j
-  // is computed, so every wave keeps one half-page of K and V in flight.
+  // two half-steps of 32 keys, each loaded into one register set and then computed. The
+  // kernel is built for 2-3 resident waves per SIMD, whose loads hide each other's
+  // latency; a second register set per wave would halve that residency.
   const int64_t first_pk = k_begin + (int64_t)kPage * wave;
   int n_half = 0;
   if (first_pk < k_end) {
@@ -167,41 +170,44 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(RB == 
 
   constexpr int kKRegs = KV == BEAM_KV_BF16 ? 8 : 4;   // 16-byte K loads per lane per half-step
   constexpr int kVRegs = KV == BEAM_KV_BF16 ? 8 : 4;   // 16-byte V loads per lane per half-step
-  u32x4_t kreg[kKRegs], vreg[kVRegs], kreg_n[kKRegs], vreg_n[kVRegs];
+  u32x4_t kreg[kKRegs], vreg[kVRegs];
 
+  // Per-lane byte offsets inside one KV head's page (loop constants, 32-bit), so every
+  // load is a uniform 64-bit page base in scalar registers plus a lane offset.
+  constexpr int kElem = KV == BEAM_KV_BF16 ? 2 : 1;
+  constexpr int kRow = kHeadDim * kElem;                  // bytes per key row
+  uint32_t koff[kKRegs], voff[kVRegs];
+  if (KV == BEAM_KV_BF16) {
+#pragma unroll
+    for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) koff[4 * sb + i] = (16 * sb + lc) * kRow + dslice<KV>(i, lg) * 2;
+#pragma unroll
+    for (int it = 0; it < 8; ++it) voff[it] = (lane / 16 + 4 * it) * kRow + lc * 16;
+  } else {
+#pragma unroll
+    for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+      for (int jj = 0; jj < 2; ++jj) koff[2 * sb + jj] = (16 * sb + lc) * kRow + 64 * jj + 16 * lg;
+#pragma unroll
+    for (int it = 0; it < 4; ++it) voff[it] = (lane / 8 + 8 * it) * kRow + (lane % 8) * 16;
+  }
+  const int64_t head_bytes = (int64_t)kPage * kRow;       // one KV head's page
   auto fetch = [&](int j, u32x4_t* kr, u32x4_t* vr) {
     const int pi = j >> 1, hs = j & 1;
     const int64_t page = page_of(pi);
-    const int64_t head_base = (page * L.Hkv + g) * head_elems;
-    if (KV == BEAM_KV_BF16) {
-      const uint16_t* kb = static_cast<const uint16_t*>(C.k) + head_base;
-      const uint16_t* vb = static_cast<const uint16_t*>(C.v) + head_base + (int64_t)(32 * hs) * kHeadDim;
+    const int64_t base = (page * L.Hkv + g) * head_bytes + (int64_t)(32 * hs) * kRow;
+    const char* kb = static_cast<const char*>(C.k) + base;
+    const char* vb = static_cast<const char*>(C.v) + base;
 #pragma unroll
-      for (int sb = 0; sb < 2; ++sb)
+    for (int i = 0; i < kKRegs; ++i) kr[i] = *reinterpret_cast<const u32x4_t*>(kb + koff[i]);
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-          kr[4 * sb + i] = *reinterpret_cast<const u32x4_t*>(
-              kb + (int64_t)(32 * hs + 16 * sb + lc) * kHeadDim + dslice<KV>(i, lg));
-#pragma unroll
-      for (int it = 0; it < 8; ++it)
-        vr[it] = *reinterpret_cast<const u32x4_t*>(vb + (int64_t)(lane / 16 + 4 * it) * kHeadDim + lc * 8);
-    } else {
-      const uint8_t* kb = static_cast<const uint8_t*>(C.k) + head_base;
-      const uint8_t* vb = static_cast<const uint8_t*>(C.v) + head_base + (int64_t)(32 * hs) * kHeadDim;
-#pragma unroll
-      for (int sb = 0; sb < 2; ++sb)
-#pragma unroll
-        for (int jj = 0; jj < 2; ++jj)
-          kr[2 * sb + jj] = *reinterpret_cast<const u32x4_t*>(
-              kb + (int64_t)(32 * hs + 16 * sb + lc) * kHeadDim + 64 * jj + 16 * lg);
-#pragma unroll
-      for (int it = 0; it < 4; ++it)
-        vr[it] = *reinterpret_cast<const u32x4_t*>(vb + (int64_t)(lane / 8 + 8 * it) * kHeadDim + (lane % 8) * 16);
-    }
+    for (int i = 0; i < kVRegs; ++i) vr[i] = *reinterpret_cast<const u32x4_t*>(vb + voff[i]);
   };
 
+
   auto compute = [&](const u32x4_t* kreg, const u32x4_t* vreg, int j) {
-    const int64_t kk0 = first_pk + (int64_t)kDecodeKeysPerBlockStep * (j >> 1) + 32 * (j & 1);
+    const int kk0 = (int)(first_pk + (int64_t)kDecodeKeysPerBlockStep * (j >> 1) + 32 * (j & 1));
     // ---- S^T = K Q^T (32 keys = 2 score blocks of 16)
     f32x4_t sc[RB][2];
 #pragma unroll
@@ -263,7 +269,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(RB == 
         for (int sb = 0; sb < 2; ++sb)
 #pragma unroll
           for (int v = 0; v < 4; ++v) {
-            const int64_t jk = kk0 + 16 * sb + 4 * lg + v;
+            const int jk = kk0 + 16 * sb + 4 * lg + v;
             if (jk > row_pos[rb] || jk < row_lo[rb]) sv[4 * sb + v] = -INFINITY;
           }
       }
@@ -272,9 +278,19 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(RB == 
       for (int e = 1; e < 8; ++e) mx = fmaxf(mx, sv[e]);
       mx = wave_xor_max(mx, 16);
       mx = wave_xor_max(mx, 32);
-      const float m_new = fmaxf(m_run[rb], mx * c);
-      const float m_use = m_new == -INFINITY ? 0.f : m_new;
-      const float alpha = __builtin_amdgcn_exp2f(m_run[rb] - m_use);
+      mx *= c;
+      // raise the running max only when some row's maximum grew by more than 2^8 (log2
+      // domain): the rescale of the output is then skipped on almost every step, and the
+      // final division by the running sum (accumulated against the same max) is exact
+      if (__builtin_amdgcn_ballot_w64(mx > m_run[rb] + kRescaleSlack) != 0) {
+        const float m_new = fmaxf(m_run[rb], mx);
+        const float alpha = m_new == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m_run[rb] - m_new);
+        l_run[rb] *= alpha;
+#pragma unroll
+        for (int d = 0; d < 8; ++d) acc[rb][d] *= alpha;
+        m_run[rb] = m_new;
+      }
+      const float m_use = m_run[rb] == -INFINITY ? 0.f : m_run[rb];
       float psum = 0.f;
       bf16x8_t pb;
 #pragma unroll
@@ -283,10 +299,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(RB == 
         psum += pe;
         pb[e] = (__bf16)pe;
       }
-      l_run[rb] = l_run[rb] * alpha + psum;
-      m_run[rb] = m_new;
-#pragma unroll
-      for (int d = 0; d < 8; ++d) acc[rb][d] *= alpha;
+      l_run[rb] += psum;
       pop[rb] = pb;
     }
     // ---- O^T += V^T P^T, V^T via transposing LDS reads
@@ -308,15 +321,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(RB == 
     }
   };
 
-  // ping-pong between two register sets: fetch the next half-step, compute this one
-  if (n_half > 0) fetch(0, kreg, vreg);
+  // one register set: fetch a half-step, compute it; other waves hide the latency
 #pragma unroll 1
-  for (int j = 0; j < n_half; j += 2) {
-    if (j + 1 < n_half) fetch(j + 1, kreg_n, vreg_n);
+  for (int j = 0; j < n_half; ++j) {
+    fetch(j, kreg, vreg);
     compute(kreg, vreg, j);
-    if (j + 1 >= n_half) break;
-    if (j + 2 < n_half) fetch(j + 2, kreg, vreg);
-    compute(kreg_n, vreg_n, j + 1);
   }
 
   // ---- merge the 4 waves of this workgroup (LDS), then write

@@ -53,6 +53,10 @@ struct DecodeSplit {
 constexpr int kDecodeWaves = 4;                       // waves per decode workgroup
 constexpr int kDecodeKeysPerBlockStep = kDecodeWaves * kPage;  // one page per wave per step
 constexpr int kDecodeMaxRowsPerChunk = 48;
+// Decode split-kernel workgroups resident per CU that its register budget is built for
+// (waves per SIMD): 3 with one 16-row block, 2 with two or three. LDS (36 KiB per
+// workgroup) admits 4.
+constexpr int decode_wgs_per_cu(int row_blocks) { return row_blocks == 1 ? 3 : 2; }
 
 hipError_t launch_qknorm_kvwrite(const LayerParams& L, const BatchParams& B, const CacheParams& C,
                                  const void* q, int64_t q_stride, const void* k, int64_t k_stride,
