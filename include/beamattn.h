@@ -43,7 +43,7 @@ extern "C" {
 typedef enum beam_status {
   BEAM_OK = 0,
   BEAM_ERR_INVALID_ARG = 1,  /* a pointer, size, stride, alignment or constant is invalid */
-  BEAM_ERR_UNSUPPORTED = 2,  /* valid but not implemented (e.g. prefill over an fp8 cache) */
+  BEAM_ERR_UNSUPPORTED = 2,  /* valid but not implemented by this library version       */
   BEAM_ERR_WORKSPACE = 3,    /* decode workspace missing or smaller than required        */
   BEAM_ERR_HIP = 4           /* the HIP runtime reported an error while launching        */
 } beam_status;
@@ -98,7 +98,13 @@ typedef struct beam_kv_cache {
  * q_start[num_seqs] = num_tokens; n_b <= max_q_len; n_b <= kv_len[b] <= max_kv_len;
  * every block_table entry for a page that holds a visible key (and, for the K/V write,
  * a new token) is in [0, num_pages). Entries for pages with no visible key are never
- * read. */
+ * read.
+ * Window-only pools for sliding layers ("Reflection Beam 1.0 on vLLM": sliding layers
+ * keep only the window's KV): several logical pages of a sequence may share one
+ * physical page, e.g. a ring of R pages with logical page p at ring page p mod R. The
+ * K/V write of a call lands before its attention reads, so a call may add at most
+ * R * page_size - window + 1 new tokens to such a sequence (65 for R = 9, page 64,
+ * window 512); then no key a new token sees has been overwritten. */
 typedef struct beam_batch {
   int32_t num_seqs;
   const int32_t* q_start;      /* device [num_seqs + 1] */
@@ -146,7 +152,10 @@ beam_status beam_qknorm_rope_ssmax_kvwrite(const beam_layer_desc* layer, const b
  * New token t at position pos sees keys [0, pos] (full) or [max(0, pos-window+1), pos]
  * (sliding), which include earlier new tokens of the same call: their K/V must already
  * be in the cache (beam_qknorm_rope_ssmax_kvwrite writes them). A query with no new
- * tokens in its sequence produces nothing. Returns BEAM_ERR_UNSUPPORTED for fp8 caches. */
+ * tokens in its sequence produces nothing. Over an fp8 cache the codes are widened
+ * exactly to bf16 on their way into the kernel's tiles; scores use sm_scale * k_scale
+ * and the output is scaled by v_scale (chunked prefill with an fp8 KV cache, "SGLang
+ * natively supports Reflection's Beam": the serving setup runs FP8 KV). */
 beam_status beam_attn_prefill(const beam_layer_desc* layer, const beam_batch* batch,
                               const beam_kv_cache* cache, const void* q, int64_t q_stride,
                               const void* gate, int64_t gate_stride, const void* gate_bias,

@@ -252,8 +252,6 @@ beam_status beam_attn_prefill(const beam_layer_desc* layer, const beam_batch* ba
   if ((s = check_layer(layer, &L)) != BEAM_OK) return s;
   if ((s = check_batch(batch, &B)) != BEAM_OK) return s;
   if ((s = check_cache(cache, &C)) != BEAM_OK) return s;
-  if (C.dtype != BEAM_KV_BF16)
-    return fail(BEAM_ERR_UNSUPPORTED, "prefill over an fp8 cache is not implemented");
   const int64_t N = B.num_tokens;
   const int64_t row = (int64_t)L.Hq * beam::kHeadDim;
   if ((s = check_tensor("q", q, q_stride, row, N)) != BEAM_OK) return s;

@@ -100,7 +100,7 @@ __device__ __forceinline__ float swap_halves_sum(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-template <int KIND>
+template <int KIND, int KV>
 __global__ __launch_bounds__(kThreads) void prefill_kernel(
     LayerParams L, BatchParams B, CacheParams C, const uint16_t* __restrict__ q, int64_t q_stride,
     const uint16_t* __restrict__ gate, int64_t gate_stride, const uint16_t* __restrict__ gate_bias,
@@ -169,7 +169,10 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(
     }
   }
 
-  const float c = L.sm_scale * kLog2e;
+  // fp8 caches: codes are converted exactly to bf16 on their way into LDS; the K scale
+  // folds into the softmax scale and the V scale into the final normalisation
+  constexpr bool fp8 = KV == BEAM_KV_FP8_E4M3;
+  const float c = L.sm_scale * kLog2e * (fp8 ? C.k_scale : 1.0f);
   float m_run = -INFINITY, l_run = 0.f;
   f32x16_t acc[4];
 #pragma unroll
@@ -216,8 +219,11 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(
   };
   int bt_cur = load_chunk(0);
   int bt_next = load_chunk(1);
-  const int64_t head_off = (int64_t)g * kTileBytes;
-  const int64_t page_bytes = (int64_t)L.Hkv * kTileBytes;
+  constexpr int kSrcTileBytes = fp8 ? kTileBytes / 2 : kTileBytes;   // one head's page in the cache
+  const int64_t head_off = (int64_t)g * kSrcTileBytes;
+  const int64_t page_bytes = (int64_t)L.Hkv * kSrcTileBytes;
+  u32x4_t k_stage = {0u, 0u, 0u, 0u}, v_stage = {0u, 0u, 0u, 0u};
+  const int fp8_off = (tid / 8) * kHeadDim + (tid % 8) * 16;   // byte offset in an fp8 page tile
   auto issue_tile = [&](int kt, auto buf_c) {
     constexpr int BUF = decltype(buf_c)::value;
     const int rel = kt - kt_begin;
@@ -229,11 +235,33 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(
     const int64_t base = (int64_t)page * page_bytes + head_off;
     const char* kb = static_cast<const char*>(C.k) + base;
     const char* vb = static_cast<const char*>(C.v) + base;
+    if constexpr (!fp8) {
 #pragma unroll
-    for (int i = 0; i < kRowsCopied / 4; ++i) {
-      const int dst = BUF * 2 * kTileBytes + (kRowsCopied * wave + 4 * i) * kRowBytes;
-      __builtin_amdgcn_global_load_lds(kb + cp_off[i], (lds_void_t*)(lds + dst), 16, 0, 0);
-      __builtin_amdgcn_global_load_lds(vb + cp_off[i], (lds_void_t*)(lds + dst + kTileBytes), 16, 0, 0);
+      for (int i = 0; i < kRowsCopied / 4; ++i) {
+        const int dst = BUF * 2 * kTileBytes + (kRowsCopied * wave + 4 * i) * kRowBytes;
+        __builtin_amdgcn_global_load_lds(kb + cp_off[i], (lds_void_t*)(lds + dst), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds(vb + cp_off[i], (lds_void_t*)(lds + dst + kTileBytes), 16, 0, 0);
+      }
+    } else {
+      // thread tid loads 16 codes (bytes 16 * (tid % 8) ..) of fp8 row tid / 8 of each
+      // tensor into registers; store_staged converts and writes them after this tile
+      k_stage = *reinterpret_cast<const u32x4_t*>(kb + fp8_off);
+      v_stage = *reinterpret_cast<const u32x4_t*>(vb + fp8_off);
+    }
+  };
+  // fp8: the staged codes of the next tile, converted to bf16, into LDS buffer BUF at the
+  // same swizzled slots the bf16 copy fills (16 codes = bf16 chunks 2j and 2j + 1)
+  auto store_staged = [&](auto buf_c) {
+    if constexpr (fp8) {
+      constexpr int BUF = decltype(buf_c)::value;
+      unsigned char* kt_lds = lds + BUF * 2 * kTileBytes;
+      const int row = tid / 8, j = tid % 8;
+      const int s0 = row * kRowBytes + (((2 * j) ^ swz_key(row)) << 4);
+      const int s1 = row * kRowBytes + (((2 * j + 1) ^ swz_key(row)) << 4);
+      *reinterpret_cast<bf16x8_t*>(kt_lds + s0) = fp8x8_to_bf16x8(k_stage[0], k_stage[1]);
+      *reinterpret_cast<bf16x8_t*>(kt_lds + s1) = fp8x8_to_bf16x8(k_stage[2], k_stage[3]);
+      *reinterpret_cast<bf16x8_t*>(kt_lds + kTileBytes + s0) = fp8x8_to_bf16x8(v_stage[0], v_stage[1]);
+      *reinterpret_cast<bf16x8_t*>(kt_lds + kTileBytes + s1) = fp8x8_to_bf16x8(v_stage[2], v_stage[3]);
     }
   };
 
@@ -358,7 +386,11 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(
       else issue_tile(kt + 1, std::integral_constant<int, 0>{});
     }
   };
-  auto finish = [&]() {
+  auto finish = [&](int kt) {
+    if (fp8 && kt + 1 < kt_end) {
+      if (buf == 0) store_staged(std::integral_constant<int, 1>{});
+      else store_staged(std::integral_constant<int, 0>{});
+    }
     __builtin_amdgcn_s_waitcnt(0);     // this wave's copies of the next tile landed
     __syncthreads();                   // ... and everyone's; this buffer is free again
     buf ^= 1;
@@ -368,17 +400,18 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(
     const int k0 = kt * kPage;
     const bool skip = !wave_active || k0 > w_max_pos || k0 + kPage - 1 < w_min_lo;
     if (!skip) compute(k0, buf, std::true_type{}, std::true_type{});
-    finish();
+    finish(kt);
   };
 
   issue_tile(kt_begin, std::integral_constant<int, 0>{});
+  store_staged(std::integral_constant<int, 0>{});
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   for (int kt = kt_begin; kt < plain_begin; ++kt) masked_step(kt);
   for (int kt = plain_begin; kt < plain_end; ++kt) {
     advance(kt);
     compute(kt * kPage, buf, std::false_type{}, std::false_type{});
-    finish();
+    finish(kt);
   }
   for (int kt = plain_end; kt < kt_end; ++kt) masked_step(kt);
 
@@ -389,7 +422,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(
   const int t = my_row / L.G;
   const int h = g * L.G + my_row % L.G;
   const int64_t tok = q0 + t;
-  const float inv = lsum > 0.f ? 1.0f / lsum : 0.f;
+  const float inv = lsum > 0.f ? (fp8 ? C.v_scale : 1.0f) / lsum : 0.f;
   const float bh = gate != nullptr ? bf16_to_f32(gate_bias[h]) : 0.f;
 #pragma unroll
   for (int db = 0; db < 4; ++db)
@@ -427,8 +460,14 @@ hipError_t launch_attn_prefill(const LayerParams& L, const BatchParams& B, const
                        static_cast<const uint16_t*>(gate_bias), static_cast<uint16_t*>(out),
                        out_stride);
   };
-  if (L.kind == BEAM_LAYER_SWA) launch(prefill_kernel<BEAM_LAYER_SWA>);
-  else launch(prefill_kernel<BEAM_LAYER_FULL>);
+  const bool f8 = C.dtype == BEAM_KV_FP8_E4M3;
+  if (L.kind == BEAM_LAYER_SWA) {
+    if (f8) launch(prefill_kernel<BEAM_LAYER_SWA, BEAM_KV_FP8_E4M3>);
+    else launch(prefill_kernel<BEAM_LAYER_SWA, BEAM_KV_BF16>);
+  } else {
+    if (f8) launch(prefill_kernel<BEAM_LAYER_FULL, BEAM_KV_FP8_E4M3>);
+    else launch(prefill_kernel<BEAM_LAYER_FULL, BEAM_KV_BF16>);
+  }
   return hipGetLastError();
 }
 

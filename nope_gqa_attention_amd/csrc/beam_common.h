@@ -129,6 +129,19 @@ __device__ __forceinline__ uint32_t f32_to_e4m3_sat(float x) {
 }
 
 // Wave-wide helpers (wave64).
+// 8 OCP e4m3 codes (two little-endian words) -> 8 bf16 values; exact (every e4m3 value
+// is a bf16 value), scale 1.
+__device__ __forceinline__ bf16x8_t fp8x8_to_bf16x8(uint32_t w0, uint32_t w1) {
+  const bf16x2_t a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, false);
+  const bf16x2_t b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, true);
+  const bf16x2_t c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, false);
+  const bf16x2_t d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, true);
+  bf16x8_t r;
+  r[0] = a[0]; r[1] = a[1]; r[2] = b[0]; r[3] = b[1];
+  r[4] = c[0]; r[5] = c[1]; r[6] = d[0]; r[7] = d[1];
+  return r;
+}
+
 __device__ __forceinline__ float wave_xor_max(float v, int mask) {
   return fmaxf(v, __shfl_xor(v, mask, 64));
 }

@@ -121,14 +121,15 @@ PREFILL_CASES = [
 ]
 
 
+@pytest.mark.parametrize("kv_dtype", ["bf16", "fp8"])
 @pytest.mark.parametrize("kind", ["swa", "full"])
 @pytest.mark.parametrize("name,q_lens,kv_lens", PREFILL_CASES, ids=[c[0] for c in PREFILL_CASES])
-def test_prefill_matches_oracle(kind, name, q_lens, kv_lens):
-    say(f"case prefill {name} kind={kind}")
-    call = synth.make_call(q_lens, kv_lens, kind, "bf16", [23, len(q_lens)])
+def test_prefill_matches_oracle(kind, name, q_lens, kv_lens, kv_dtype):
+    say(f"case prefill {name} kind={kind} kv={kv_dtype}")
+    call = synth.make_call(q_lens, kv_lens, kind, kv_dtype, [23, len(q_lens)])
     ref = O.layer_call(call.oracle_inputs())
     d = run_layer(call, mode="prefill")
-    assert_close_to_oracle(bits16(d["out"]), ref["y"], "bf16", f"prefill {name} {kind}")
+    assert_close_to_oracle(bits16(d["out"]), ref["y"], kv_dtype, f"prefill {name} {kind} {kv_dtype}")
 
 
 @pytest.mark.parametrize("kind", ["swa", "full"])
@@ -223,10 +224,10 @@ def test_invalid_arguments_return_status_and_launch_nothing():
     with pytest.raises(ba.BeamError) as e:
         ba.beam_attn_prefill(bad, d["batch"], d["cache"], d["q"], d["gate"], d["gate_bias"], d["out"])
     assert e.value.status == ba.BEAM_ERR_INVALID_ARG and "head_dim" in str(e.value)
-    fp8 = ba.DeviceCache(torch.zeros_like(d["cache"].k, dtype=torch.uint8), torch.zeros_like(d["cache"].v, dtype=torch.uint8), 0.1, 0.1)
+    fp8 = ba.DeviceCache(torch.zeros_like(d["cache"].k, dtype=torch.uint8), torch.zeros_like(d["cache"].v, dtype=torch.uint8), 0.1, 0.0)
     with pytest.raises(ba.BeamError) as e:
         ba.beam_attn_prefill(d["layer"].desc, d["batch"], fp8, d["q"], d["gate"], d["gate_bias"], d["out"])
-    assert e.value.status == ba.BEAM_ERR_UNSUPPORTED
+    assert e.value.status == ba.BEAM_ERR_INVALID_ARG and "scale" in str(e.value)
     big = synth.make_call([20], [100], "full", "bf16", [28, 1])
     db = stage(big)
     with pytest.raises(ba.BeamError) as e:
