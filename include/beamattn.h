@@ -95,7 +95,12 @@ typedef struct beam_kv_cache {
  * writes use one contract): token pos of sequence b lives in physical page
  * block_table[b * max_pages + pos / page_size] at slot pos % page_size.
  * Preconditions on the device arrays: q_start is non-decreasing with q_start[0] = 0 and
- * q_start[num_seqs] = num_tokens; n_b <= max_q_len; n_b <= kv_len[b] <= max_kv_len;
+ * q_start[num_seqs] <= num_tokens; n_b <= max_q_len; n_b <= kv_len[b] <= max_kv_len.
+ * Rows q_start[num_seqs] .. num_tokens-1 are padding: no K/V is stored for them and no
+ * attention output is written for them (beam_head_gate, which has no batch, gates them
+ * like any row). With padding and host bounds that cover every step (max_q_len,
+ * max_kv_len, max_pages), one recorded HIP graph of a decode step replays for any
+ * lengths within the bounds: only the device arrays and tensor contents change.
  * every block_table entry for a page that holds a visible key (and, for the K/V write,
  * a new token) is in [0, num_pages). Entries for pages with no visible key are never
  * read.
@@ -113,7 +118,7 @@ typedef struct beam_batch {
   int32_t max_pages;           /* row stride of block_table; >= ceil(max_kv_len / page_size) */
   int32_t max_q_len;           /* host bound on n_b */
   int64_t max_kv_len;          /* host bound on kv_len[b] */
-  int64_t num_tokens;          /* q_start[num_seqs] */
+  int64_t num_tokens;          /* rows of the token-indexed tensors, >= q_start[num_seqs] */
 } beam_batch;
 
 /* Fused per-head Q/K RMSNorm + RoPE (sliding layer) or SSMax query scaling (full layer)

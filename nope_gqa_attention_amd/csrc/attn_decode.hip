@@ -406,6 +406,7 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(
   const int64_t tok = row / L.Hq;
   const int h = (int)(row % L.Hq);
   const int wave = threadIdx.x / 64, lane = threadIdx.x % 64;
+  if (tok >= B.q_start[B.num_seqs]) return;      // padding row past the last sequence
   const int b = seq_of_token(B.q_start, B.num_seqs, tok);
   const int64_t n = (int64_t)B.q_start[b + 1] - B.q_start[b];
   const int64_t kv = B.kv_len[b];

@@ -36,6 +36,7 @@ __global__ __launch_bounds__(kThreads) void qknorm_kvwrite_kernel(
 
   const int64_t t = blockIdx.x;                 // token index in call order
   const int tid = threadIdx.x;
+  if (t >= B.q_start[B.num_seqs]) return;       // padding row past the last sequence
 
   // sequence of token t: last b with q_start[b] <= t (q_start non-decreasing)
   int lo = 0, hi = B.num_seqs - 1;

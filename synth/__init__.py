@@ -116,7 +116,8 @@ class LayerCall:
 
 
 def make_call(q_lens, kv_lens, kind: str, kv_dtype: str, seed, name: str = "case",
-              spare_pages: int = 3, window: int = WINDOW, cache_device=None) -> LayerCall:
+              spare_pages: int = 3, window: int = WINDOW, cache_device=None,
+              fp8_scales=None) -> LayerCall:
     """A layer call with the given new-token counts and total key counts per sequence.
 
     Draw order: page permutation, q, k, v, gate, q_norm_w, k_norm_w, gate_bias,
@@ -124,7 +125,8 @@ def make_call(q_lens, kv_lens, kind: str, kv_dtype: str, seed, name: str = "case
     "cuda"), the cached K/V are drawn on that device by torch's seeded Philox generator
     instead of numpy (same distributions, different values, much faster for the
     multi-GiB caches); everything else is unchanged. The returned caches then live on
-    that device.
+    that device. fp8_scales = (k_scale, v_scale) fixes the fp8 scales instead of
+    amax / 448 of the drawn cache (so that several calls can share one cache descriptor).
     """
     q_lens = np.asarray(q_lens, dtype=np.int64)
     kv_lens = np.asarray(kv_lens, dtype=np.int64)
@@ -192,8 +194,11 @@ def make_call(q_lens, kv_lens, kind: str, kv_dtype: str, seed, name: str = "case
         kc[un_p, :, un_s, :] = nan
         vc[un_p, :, un_s, :] = nan
     elif kv_dtype == "fp8":
-        k_scale = float(np.float32(max(_amax(kc), 1e-3) / 448.0))
-        v_scale = float(np.float32(max(_amax(vc), 1e-3) / 448.0))
+        if fp8_scales is None:
+            k_scale = float(np.float32(max(_amax(kc), 1e-3) / 448.0))
+            v_scale = float(np.float32(max(_amax(vc), 1e-3) / 448.0))
+        else:
+            k_scale, v_scale = (float(np.float32(x)) for x in fp8_scales)
         kc = _fp8_codes(kc, k_scale)
         vc = _fp8_codes(vc, v_scale)
         kc[un_p, :, un_s, :] = FP8_NAN
