@@ -81,14 +81,15 @@ def summarize_counters(paths):
             gb = (fm * factor["FETCH_SIZE"] + wm * factor["WRITE_SIZE"]) * 1024 / 1e9
         lines.append(f"| {k} | {max(len(f), len(w))} | {fm if fm is None else round(fm, 1)} | "
                      f"{wm if wm is None else round(wm, 1)} | {gb if gb is None else round(gb, 3)} |")
-        if k.endswith("prefill_kernel<1>") and gb is not None:
+        # the full NoPE layer over a bf16 cache: prefill_kernel<BEAM_LAYER_FULL, BEAM_KV_BF16>
+        if re.search(r"prefill_kernel<1(, 0)?>$", k) and gb is not None:
             record = round(gb * 1e9)
     lines.append("")
     lines.append(f"calibration (1 GiB copy): FETCH_SIZE {calib.get('FETCH_SIZE')} KiB -> factor "
                  f"{round(factor.get('FETCH_SIZE', 0), 4)}; WRITE_SIZE {calib.get('WRITE_SIZE')} KiB "
                  f"-> factor {round(factor.get('WRITE_SIZE', 0), 4)}")
     if record is not None:
-        lines.append(f"traffic-record: kernel=prefill_kernel<1> bytes_per_launch={record} "
+        lines.append(f"traffic-record: kernel=prefill_kernel<1,0> bytes_per_launch={record} "
                      f"source_sha256={file_sha256(PREFILL_SRC)}")
     return "\n".join(lines)
 
