@@ -76,3 +76,30 @@ def assert_close_to_oracle(gpu_out_bits, y_ref, kv_dtype, what=""):
         f"rows {g.shape[0]}")
     assert mx <= tmax and mean <= tmean, f"{what}: max {mx} mean {mean}"
     return mx, mean
+
+
+def seq_host_inputs(call, b: int):
+    """Oracle inputs for sequence b of a (possibly device-resident, multi-GiB) call: only
+    the pages its block table names are copied to the host, renumbered densely, so the
+    oracle reads exactly the bytes the GPU read."""
+    bt = np.asarray(call.block_table[b])
+    pages, inv = np.unique(bt, return_inverse=True)
+    idx = torch.from_numpy(pages.astype(np.int64)).to(call.k_cache.device)
+    kc = call.k_cache[idx].cpu()
+    vc = call.v_cache[idx].cpu()
+    s, e = int(call.q_start[b]), int(call.q_start[b + 1])
+
+    def bits(t):
+        t = t.cpu()
+        return t.view(torch.int16).numpy().view(np.uint16) if t.dtype == torch.bfloat16 else t.numpy()
+
+    return {
+        "kind": call.kind, "kv_dtype": call.kv_dtype,
+        "q_start": np.array([0, e - s], dtype=np.int32), "kv_len": np.asarray(call.kv_len[b:b + 1]),
+        "block_table": inv.astype(np.int32).reshape(1, -1),
+        "q": bits(call.q[s:e]), "k": bits(call.k[s:e]), "v": bits(call.v[s:e]),
+        "gate": bits(call.gate[s:e]), "q_norm_w": bits(call.q_norm_w),
+        "k_norm_w": bits(call.k_norm_w), "gate_bias": bits(call.gate_bias),
+        "k_cache": bits(kc), "v_cache": bits(vc),
+        "k_scale": call.k_scale, "v_scale": call.v_scale,
+    }
