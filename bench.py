@@ -310,6 +310,29 @@ def run_decode(args, result):
 
 
 
+def run_projections(args, result, m):
+    """The sublayer projections around the attention core at the long-prefill token count:
+    packed Q/K/V/gate (5120 -> 14336) and o_proj (6144 -> 5120), y = x W^T in bf16 with
+    fp32 accumulation (MFMA-bound at this size)."""
+    import torch
+
+    import synth
+    from nope_gqa_attention_amd import beamattn as ba
+
+    proj = {}
+    for name, n, k in (("qkv_gate", 14336, 5120), ("o_proj", 5120, 6144)):
+        x, w = synth.make_linear(m, n, k, [83, n, k], device="cuda")
+        y = torch.empty(m, n, dtype=torch.bfloat16, device="cuda")
+        _, per = timed_steps([("gemm", lambda: ba.beam_linear_bf16(x, w, y))], args.steps, args.warmup)
+        tf = 2.0 * m * n * k / (per["gemm"] * 1e-3) / 1e12
+        proj[name] = {"m": m, "n": n, "k": k, "ms": round(per["gemm"], 4), "tflops": round(tf, 1),
+                      "mfma_frac": round(tf / PEAK_BF16_TFLOPS, 4)}
+        log(f"  projection {name}: {proj[name]}")
+        del x, w, y
+        torch.cuda.empty_cache()
+    result["projections"] = proj
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -425,6 +448,8 @@ def main():
 
     if not args.no_decode and args.only == "all":  # "--only prefill" skips the decode workloads
         run_decode(args, result)
+    if args.only in ("all", "prefill"):
+        run_projections(args, result, new_tokens)
 
     # ---------------------------------------------------------------- oracle on the host
     if not args.no_cpu_baseline:

@@ -38,7 +38,7 @@
 extern "C" {
 #endif
 
-#define BEAM_ABI_VERSION 1
+#define BEAM_ABI_VERSION 2
 
 typedef enum beam_status {
   BEAM_OK = 0,
@@ -194,6 +194,23 @@ beam_status beam_head_gate(const beam_layer_desc* layer, int64_t num_tokens,
                            const void* attn, int64_t attn_stride,
                            const void* gate, int64_t gate_stride, const void* gate_bias,
                            void* out, int64_t out_stride, void* stream);
+
+/* bf16 linear layer y = x W^T for the projections on either side of the attention core:
+ * the packed Q/K/V/gate projection (hidden 5120 -> 14336 = 6144 q + 1024 k + 1024 v + 6144
+ * gate columns; "Agent-driven optimization" of the vLLM page: one packed GEMM feeds the
+ * fused norm kernel, whose strided inputs are column ranges of its output) and o_proj
+ * (6144 -> 5120). y[i][j] = bf16(sum_c x[i][c] * w[j][c]) with fp32 accumulation.
+ *  m, n, k  rows of x (tokens), output features, input features; k % 64 == 0, n % 4 == 0
+ *  x        device bf16 [m][k], row stride x_stride (>= k, a multiple of 8)
+ *  w        device bf16 [n][k] (the weight in its [out][in] layout), row stride w_stride
+ *           (>= k, a multiple of 8)
+ *  y        device bf16 [m][n], row stride y_stride (>= n, a multiple of 8); must not
+ *           overlap x or w
+ * m == 0 launches nothing. Sized for prefill token counts (tiles of 256 tokens x 256
+ * features); it is correct for any m. */
+beam_status beam_linear_bf16(int64_t m, int64_t n, int64_t k, const void* x, int64_t x_stride,
+                             const void* w, int64_t w_stride, void* y, int64_t y_stride,
+                             void* stream);
 
 /* KV-cache bytes that grow with each token (the "Attention" section of the vLLM pages):
  * num_full_layers * 2 (K and V) * num_kv_heads * head_dim * bytes per value; only the

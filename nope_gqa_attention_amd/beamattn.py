@@ -18,14 +18,15 @@ import torch
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libbeamattn.so")
 
-BEAM_ABI_VERSION = 1
+BEAM_ABI_VERSION = 2
 BEAM_OK, BEAM_ERR_INVALID_ARG, BEAM_ERR_UNSUPPORTED, BEAM_ERR_WORKSPACE, BEAM_ERR_HIP = range(5)
 BEAM_LAYER_SWA, BEAM_LAYER_FULL = 0, 1
 BEAM_KV_BF16, BEAM_KV_FP8_E4M3 = 0, 1
 
 ENTRY_POINTS = (
     "beam_qknorm_rope_ssmax_kvwrite", "beam_attn_prefill", "beam_attn_decode",
-    "beam_attn_decode_workspace_bytes", "beam_head_gate", "beam_kv_bytes_per_token",
+    "beam_attn_decode_workspace_bytes", "beam_head_gate", "beam_linear_bf16",
+    "beam_kv_bytes_per_token",
     "beam_status_string", "beam_last_error", "beam_abi_version",
 )
 
@@ -101,6 +102,9 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         P(LayerDesc), c_int64, c_void_p, c_int64, c_void_p, c_int64, c_void_p, c_void_p, c_int64,
         c_void_p]
     lib.beam_head_gate.restype = c_int32
+    lib.beam_linear_bf16.argtypes = [c_int64, c_int64, c_int64, c_void_p, c_int64, c_void_p,
+                                     c_int64, c_void_p, c_int64, c_void_p]
+    lib.beam_linear_bf16.restype = c_int32
     lib.beam_kv_bytes_per_token.argtypes = [c_int32, c_int32, c_int32, c_int32]
     lib.beam_kv_bytes_per_token.restype = c_uint64
     lib.beam_status_string.argtypes = [c_int32]
@@ -260,6 +264,21 @@ def beam_head_gate(layer: LayerDesc, attn, gate, gate_bias, out, stream=None):
     n = attn.shape[0]
     _check(lib.beam_head_gate(ctypes.byref(layer), n, ap, as_, gp, gs,
                               c_void_p(gate_bias.data_ptr()), op, os_, _stream(stream)))
+
+
+def beam_linear_bf16(x, w, y, stream=None):
+    """y = x w^T: x [m, k], w [n, k], y [m, n] bf16 CUDA tensors with unit column stride
+    (row strides free, e.g. column ranges of a wider tensor)."""
+    for name, t in (("x", x), ("w", w), ("y", y)):
+        if t.dtype != torch.bfloat16 or t.dim() != 2 or t.stride(1) != 1 or not t.is_cuda:
+            raise ValueError(f"{name} must be a 2-D bf16 CUDA tensor with unit column stride")
+    m, k = x.shape
+    n = w.shape[0]
+    if w.shape[1] != k or tuple(y.shape) != (m, n):
+        raise ValueError(f"shape mismatch: x {tuple(x.shape)}, w {tuple(w.shape)}, y {tuple(y.shape)}")
+    _check(load().beam_linear_bf16(m, n, k, c_void_p(x.data_ptr()), x.stride(0),
+                                   c_void_p(w.data_ptr()), w.stride(0), c_void_p(y.data_ptr()),
+                                   y.stride(0), _stream(stream)))
 
 
 def beam_kv_bytes_per_token(num_full_layers: int, num_kv_heads: int, head_dim: int, dtype: int) -> int:

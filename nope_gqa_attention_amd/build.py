@@ -21,7 +21,8 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(HERE, "_build")
 LIB_PATH = os.path.join(HERE, "libbeamattn.so")
-SOURCES = ["api.cpp", "qknorm_kvwrite.hip", "head_gate.hip", "attn_decode.hip", "attn_prefill.hip"]
+SOURCES = ["api.cpp", "qknorm_kvwrite.hip", "head_gate.hip", "attn_decode.hip", "attn_prefill.hip",
+           "linear.hip"]
 ARCH = "gfx950"
 
 

@@ -332,6 +332,28 @@ beam_status beam_head_gate(const beam_layer_desc* layer, int64_t num_tokens, con
                                          static_cast<hipStream_t>(stream)));
 }
 
+beam_status beam_linear_bf16(int64_t m, int64_t n, int64_t k, const void* x, int64_t x_stride,
+                             const void* w, int64_t w_stride, void* y, int64_t y_stride,
+                             void* stream) {
+  if (m < 0 || n <= 0 || k <= 0) return fail(BEAM_ERR_INVALID_ARG, "linear needs m >= 0, n > 0, k > 0");
+  if (k % 64 != 0) return fail(BEAM_ERR_INVALID_ARG, "linear k (%lld) must be a multiple of 64", (long long)k);
+  if (n % 4 != 0) return fail(BEAM_ERR_INVALID_ARG, "linear n (%lld) must be a multiple of 4", (long long)n);
+  if (m > 0x7FFFFFFFLL || n > 0x7FFFFFFFLL || k > 0x7FFFFFFFLL)
+    return fail(BEAM_ERR_INVALID_ARG, "linear dimensions must fit in 31 bits");
+  beam_status s;
+  if ((s = check_tensor("x", x, x_stride, k, m)) != BEAM_OK) return s;
+  if ((s = check_tensor("w", w, w_stride, k, n)) != BEAM_OK) return s;
+  if ((s = check_tensor("y", y, y_stride, n, m)) != BEAM_OK) return s;
+  if (m > 0) {
+    const int64_t xb = ((m - 1) * x_stride + k) * 2, wb = ((n - 1) * w_stride + k) * 2,
+                  yb = ((m - 1) * y_stride + n) * 2;
+    if (ranges_overlap(y, yb, x, xb) || ranges_overlap(y, yb, w, wb))
+      return fail(BEAM_ERR_INVALID_ARG, "linear y must not overlap x or w");
+  }
+  return launched(beam::launch_linear_bf16(m, n, k, x, x_stride, w, w_stride, y, y_stride,
+                                           static_cast<hipStream_t>(stream)));
+}
+
 uint64_t beam_kv_bytes_per_token(int32_t num_full_layers, int32_t num_kv_heads, int32_t head_dim,
                                  int32_t dtype) {
   if (num_full_layers < 0 || num_kv_heads < 0 || head_dim < 0) return 0;

@@ -64,6 +64,10 @@ hipError_t launch_qknorm_kvwrite(const LayerParams& L, const BatchParams& B, con
                                  const void* k_norm_w, int64_t norm_w_head_stride, void* q_out,
                                  int64_t q_out_stride, hipStream_t stream);
 
+hipError_t launch_linear_bf16(int64_t M, int64_t N, int64_t K, const void* x, int64_t x_stride,
+                              const void* w, int64_t w_stride, void* y, int64_t y_stride,
+                              hipStream_t stream);
+
 hipError_t launch_head_gate(const LayerParams& L, int64_t num_tokens, const void* attn,
                             int64_t attn_stride, const void* gate, int64_t gate_stride,
                             const void* gate_bias, void* out, int64_t out_stride,

@@ -407,6 +407,20 @@ def head_gate(o, gate_bits, bias_bits):
 
 
 # ----------------------------------------------------------------------------------
+# Projections on either side of the core ([P5] Attention: the gate has its own
+# full-width projection; [P2] Agent-driven optimization: one packed GEMM feeds the fused
+# norm kernel; o_proj after the gate)
+# ----------------------------------------------------------------------------------
+
+def linear(x_bits, w_bits) -> np.ndarray:
+    """y = x W^T in fp64 from bf16 inputs: x [m, k], W [n, k] (the weight in its [out][in]
+    layout), so y[i, j] = sum_c x[i, c] * W[j, c]. The packed projection maps the 5120
+    hidden values to 6144 q + 1024 k + 1024 v + 6144 gate columns; o_proj maps the 6144
+    gated attention values back to 5120. Exact products and an fp64 sum; no rounding."""
+    return np.matmul(bf16_bits_to_f64(x_bits), bf16_bits_to_f64(w_bits).T)
+
+
+# ----------------------------------------------------------------------------------
 # KV-cache size closed form [P2, Attention] / [P5, Attention: ...] / [P4]
 # ----------------------------------------------------------------------------------
 

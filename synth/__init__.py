@@ -296,3 +296,19 @@ def make_config(cfg: int, kind: str, seed: int | None = None, cache_device=None)
                      name=f"config{cfg}-{kind}", cache_device=cache_device)
     call.extra["description"] = desc
     return call
+
+
+def make_linear(m: int, n: int, k: int, seed, device=None):
+    """Inputs of one projection y = x W^T: x [m, k] ~ N(0,1) and W [n, k] ~ N(0,1)/sqrt(k),
+    both rounded to bf16 by torch's cast (so y has unit scale). With device set, both are
+    drawn there by torch's seeded generator."""
+    key = [int(s) for s in (seed if isinstance(seed, (list, tuple)) else [seed])]
+    if device is None:
+        x = _bf16(_normal_f32(m * k, key + [1])).view(m, k)
+        w = _bf16(_normal_f32(n * k, key + [2]) / np.float32(math.sqrt(k))).view(n, k)
+        return x, w
+    g = torch.Generator(device=device)
+    g.manual_seed(int(np.random.default_rng(key + [1]).integers(1 << 62)))
+    x = torch.randn(m, k, generator=g, device=device, dtype=torch.float32).to(torch.bfloat16)
+    w = (torch.randn(n, k, generator=g, device=device, dtype=torch.float32) / math.sqrt(k)).to(torch.bfloat16)
+    return x, w

@@ -489,3 +489,43 @@ def test_long_context_path_equals_short_path():
     b2 = O.attention_rows_long(q, kc, vc, inp["block_table"], seq, pos, "swa", "bf16", key_chunk=100)
     np.testing.assert_allclose(a2, b2, atol=1e-13, rtol=0)
     np.testing.assert_allclose(a, b, atol=1e-13, rtol=0)
+
+
+# ------------------------------------------------------------------ projections
+
+def _bits(t):
+    return t.view(torch.int16).numpy().view(np.uint16)
+
+
+def test_linear_equals_exact_rational_sum_on_small_shapes():
+    """y[i, j] = sum_c x[i, c] W[j, c]: every term is an exact product of two bf16 values,
+    summed here in exact rationals; the fp64 oracle may differ only by its own rounding."""
+    x, w = synth.make_linear(3, 5, 64, [71, 0])
+    y = O.linear(_bits(x), _bits(w))
+    xf = [[Fraction(float(v)) for v in row] for row in x.float().numpy()]
+    wf = [[Fraction(float(v)) for v in row] for row in w.float().numpy()]
+    for i in range(3):
+        for j in range(5):
+            exact = sum(a * b for a, b in zip(xf[i], wf[j]))
+            mass = sum(abs(a * b) for a, b in zip(xf[i], wf[j]))
+            assert abs(Fraction(y[i, j]) - exact) <= mass * Fraction(64, 2 ** 53)
+
+
+def test_linear_identity_permutation_and_row_sums():
+    x, _ = synth.make_linear(4, 8, 64, [72, 0])
+    one = torch.eye(64, dtype=torch.bfloat16)
+    assert np.array_equal(O.linear(_bits(x), _bits(one)), x.double().numpy())
+    perm = torch.from_numpy(np.random.default_rng(3).permutation(64))
+    y = O.linear(_bits(x), _bits(one[perm]))
+    assert np.array_equal(y, x.double().numpy()[:, perm.numpy()])          # column j is x[:, perm[j]]
+    ones = torch.ones(1, 64, dtype=torch.bfloat16)
+    np.testing.assert_allclose(O.linear(_bits(x), _bits(ones))[:, 0], x.double().numpy().sum(axis=1),
+                               rtol=0, atol=1e-12)
+
+
+def test_linear_orientation_is_x_times_w_transposed():
+    """A transposed operand would fail on shapes where only x W^T is defined."""
+    x, w = synth.make_linear(3, 7, 128, [73, 0])
+    y = O.linear(_bits(x), _bits(w))
+    assert y.shape == (3, 7)
+    np.testing.assert_allclose(y, x.double().numpy() @ w.double().numpy().T, rtol=0, atol=1e-12)
