@@ -16,8 +16,9 @@
 //    the accumulator then holds 4 consecutive n per lane, stored as 8 bytes).
 //  * K advances 64 at a time through LDS: 256 rows x 128 bytes of each operand per stage
 //    (64 KiB), copied straight from global memory with global_load_lds_dwordx4 and
-//    double-buffered. The 16-byte chunk c of row r is stored at slot c ^ (r mod 8), so the
-//    operand reads (32 rows at one chunk) hit distinct banks.
+//    double-buffered. gfx950's LDS has 64 four-byte banks, so two 128-byte rows fill them;
+//    the 16-byte chunk c of row r is stored at slot c ^ ((r / 2) mod 8), so the 16 rows a
+//    16-lane group of an operand read touches (one chunk each) cover all 64 banks.
 //  * Workgroups are remapped so that each XCD runs a contiguous range of tiles, ordered
 //    4 m-tiles at a time: the ~32 workgroups an XCD runs together cover a 4 x 8 block of
 //    tiles and share each x and W slab through its L2.
@@ -62,13 +63,13 @@ __global__ __launch_bounds__(kLinThreads) void linear_bf16_kernel(
 
   // ---- copy of one stage: wave w moves rows [32w, 32w + 32) of both tiles, 8 rows per
   // instruction; lane l lands at row 8i + l/8, slot l%8, so it fetches that row's chunk
-  // (l%8) ^ (row%8). Rows past M or N read the last valid row (their results are dropped).
+  // (l%8) ^ ((row/2)%8). Rows past M or N read the last valid row (their results are dropped).
   const int64_t nk = K / kBK;
   int64_t wrow_off[4], xrow_off[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int row = 32 * wave + 8 * i + lane / 8;
-    const int chunk = (lane % 8) ^ (row % 8);
+    const int chunk = (lane % 8) ^ ((row >> 1) & 7);
     const int64_t wr = min(n0 + row, N - 1), xr = min(m0 + row, M - 1);
     wrow_off[i] = wr * w_stride * 2 + chunk * 16;
     xrow_off[i] = xr * x_stride * 2 + chunk * 16;
@@ -85,10 +86,10 @@ __global__ __launch_bounds__(kLinThreads) void linear_bf16_kernel(
   };
 
   // ---- operand offsets: row lr of a 32-row block, chunk 2*kk + half at slot
-  // (2*kk + half) ^ (lr % 8) (block starts are multiples of 32 rows)
+  // (2*kk + half) ^ ((lr/2) % 8) (block starts are multiples of 32 rows)
   int op_off[4];
 #pragma unroll
-  for (int kk = 0; kk < 4; ++kk) op_off[kk] = lr * kLinRowBytes + (((2 * kk + half) ^ (lr % 8)) << 4);
+  for (int kk = 0; kk < 4; ++kk) op_off[kk] = lr * kLinRowBytes + (((2 * kk + half) ^ ((lr >> 1) & 7)) << 4);
 
   f32x16_t acc[2][4];
 #pragma unroll
