@@ -142,7 +142,8 @@ class Staged:
         self.batch = ba.DeviceBatch(call.q_start, call.kv_len, call.block_table, device)
         self.cache = ba.DeviceCache(call.k_cache.to(device), call.v_cache.to(device),
                                     call.k_scale, call.v_scale)
-        self.layer = HybridAttention(call.kind)
+        self.layer = HybridAttention(call.kind, num_q_heads=call.num_q_heads,
+                                     num_kv_heads=call.num_kv_heads)
         for n in ("q", "k", "v", "gate", "q_norm_w", "k_norm_w", "gate_bias"):
             setattr(self, n, getattr(call, n).to(device))
         self.q_out = torch.empty_like(self.q)
@@ -310,6 +311,40 @@ def run_decode(args, result):
 
 
 
+def run_head_share(args, result):
+    """The share of one of 8 GPUs that split the heads (1 KV head, 6 query heads, its own
+    pages): the long prefill (full and SWA layers) and the batch-1 decode and 1M-key verify
+    (full layer), at their real per-GPU shapes."""
+    import torch
+
+    import synth
+
+    hq, hkv = 6, 1
+    share = {}
+    for cfg, kind in ((1, "full"), (1, "swa"), (2, "full"), (4, "full")):
+        call = synth.make_config(cfg, kind, cache_device="cuda", heads=(hq, hkv))
+        s = Staged(call)
+        ql = [int(x) for x in call.q_lens]
+        kl = [int(x) for x in call.kv_len]
+        mode = "prefill" if cfg == 1 else "decode"
+        _, per = timed_steps([("kvwrite", s.kvwrite), ("attn", lambda s=s, mode=mode: s.attend(mode))],
+                             max(args.steps, 5), args.warmup)
+        entry = {"q_heads": hq, "kv_heads": hkv, "attn_ms": round(per["attn"], 4),
+                 "kvwrite_ms": round(per["kvwrite"], 4)}
+        if mode == "prefill":
+            tf = 4 * D * hq * visible_pairs(ql, kl, kind) / (per["attn"] * 1e-3) / 1e12
+            entry.update({"tflops": round(tf, 1), "mfma_frac": round(tf / PEAK_BF16_TFLOPS, 4)})
+        else:
+            nbytes = visible_keys_decode(ql, kl, kind) * 2 * hkv * D * (2 if call.kv_dtype == "bf16" else 1)
+            gbs = nbytes / (per["attn"] * 1e-3) / 1e9
+            entry.update({"kv_bytes": nbytes, "hbm_gbs": round(gbs, 1), "hbm_frac": round(gbs / PEAK_HBM_GBS, 4)})
+        share[f"config{cfg}-{kind}"] = entry
+        log(f"  head share config{cfg}-{kind}: {entry}")
+        del s, call
+        torch.cuda.empty_cache()
+    result["head_share_tp8"] = share
+
+
 def run_projections(args, result, m):
     """The sublayer projections around the attention core at the long-prefill token count:
     packed Q/K/V/gate (5120 -> 14336) and o_proj (6144 -> 5120), y = x W^T in bf16 with
@@ -448,6 +483,7 @@ def main():
 
     if not args.no_decode and args.only == "all":  # "--only prefill" skips the decode workloads
         run_decode(args, result)
+        run_head_share(args, result)
     if args.only in ("all", "prefill"):
         run_projections(args, result, new_tokens)
 

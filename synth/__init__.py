@@ -64,19 +64,27 @@ class LayerCall:
     q_start: np.ndarray            # int32 [B+1]
     kv_len: np.ndarray             # int32 [B], keys after this call (new ones included)
     block_table: np.ndarray        # int32 [B, max_pages]
-    q: torch.Tensor                # bf16 [N, 48, 128]
-    k: torch.Tensor                # bf16 [N, 8, 128]
-    v: torch.Tensor                # bf16 [N, 8, 128]
-    gate: torch.Tensor             # bf16 [N, 6144]
+    q: torch.Tensor                # bf16 [N, Hq, 128] (Hq = 48 unless heads is given)
+    k: torch.Tensor                # bf16 [N, Hkv, 128] (Hkv = 8 unless heads is given)
+    v: torch.Tensor                # bf16 [N, Hkv, 128]
+    gate: torch.Tensor             # bf16 [N, Hq * 128]
     q_norm_w: torch.Tensor         # bf16 [128]
     k_norm_w: torch.Tensor         # bf16 [128]
-    gate_bias: torch.Tensor        # bf16 [48]
-    k_cache: torch.Tensor          # bf16 or uint8 [num_pages, 8, 64, 128]
+    gate_bias: torch.Tensor        # bf16 [Hq]
+    k_cache: torch.Tensor          # bf16 or uint8 [num_pages, Hkv, 64, 128]
     v_cache: torch.Tensor
     k_scale: float = 1.0
     v_scale: float = 1.0
     poison_page: int = -1
     extra: dict = field(default_factory=dict)
+
+    @property
+    def num_q_heads(self) -> int:
+        return int(self.q.shape[1])
+
+    @property
+    def num_kv_heads(self) -> int:
+        return int(self.k.shape[1])
 
     @property
     def num_seqs(self) -> int:
@@ -117,7 +125,7 @@ class LayerCall:
 
 def make_call(q_lens, kv_lens, kind: str, kv_dtype: str, seed, name: str = "case",
               spare_pages: int = 3, window: int = WINDOW, cache_device=None,
-              fp8_scales=None) -> LayerCall:
+              fp8_scales=None, heads=None) -> LayerCall:
     """A layer call with the given new-token counts and total key counts per sequence.
 
     Draw order: page permutation, q, k, v, gate, q_norm_w, k_norm_w, gate_bias,
@@ -127,7 +135,11 @@ def make_call(q_lens, kv_lens, kind: str, kv_dtype: str, seed, name: str = "case
     multi-GiB caches); everything else is unchanged. The returned caches then live on
     that device. fp8_scales = (k_scale, v_scale) fixes the fp8 scales instead of
     amax / 448 of the drawn cache (so that several calls can share one cache descriptor).
+    heads = (Hq, Hkv) replaces the 48 query and 8 KV heads, e.g. (6, 1) for the share of
+    one of 8 GPUs that split the heads.
     """
+    hq, hkv = (HQ, HKV) if heads is None else (int(heads[0]), int(heads[1]))
+    assert hq > 0 and hkv > 0 and hq % hkv == 0
     q_lens = np.asarray(q_lens, dtype=np.int64)
     kv_lens = np.asarray(kv_lens, dtype=np.int64)
     assert np.all(q_lens >= 0) and np.all(kv_lens >= q_lens)
@@ -157,18 +169,18 @@ def make_call(q_lens, kv_lens, kind: str, kv_dtype: str, seed, name: str = "case
             cursor += 1
 
     N = int(q_lens.sum())
-    q = _bf16(_normal_f32(N * HQ * D, key + [2])).view(N, HQ, D)
-    k = _bf16(_normal_f32(N * HKV * D, key + [3])).view(N, HKV, D)
-    v = _bf16(_normal_f32(N * HKV * D, key + [4])).view(N, HKV, D)
-    gate = _bf16(_normal_f32(N * HQ * D, key + [5])).view(N, HQ * D)
+    q = _bf16(_normal_f32(N * hq * D, key + [2])).view(N, hq, D)
+    k = _bf16(_normal_f32(N * hkv * D, key + [3])).view(N, hkv, D)
+    v = _bf16(_normal_f32(N * hkv * D, key + [4])).view(N, hkv, D)
+    gate = _bf16(_normal_f32(N * hq * D, key + [5])).view(N, hq * D)
     q_norm_w = _bf16(1.0 + 0.1 * _normal_f32(D, key + [6]))
     k_norm_w = _bf16(1.0 + 0.1 * _normal_f32(D, key + [7]))
-    gate_bias = _bf16(_normal_f32(HQ, key + [8]))
+    gate_bias = _bf16(_normal_f32(hq, key + [8]))
 
     # Cached K/V: N(0,1) values at every slot of every page, then NaN at the slots
     # that hold no cached token yet (new tokens' slots, tails, the shared NaN page).
-    shape = (num_pages, HKV, PAGE, D)
-    n_cache = num_pages * HKV * PAGE * D
+    shape = (num_pages, hkv, PAGE, D)
+    n_cache = num_pages * hkv * PAGE * D
     if cache_device is None:
         kc = _normal_bf16(n_cache, key + [9]).view(shape)
         vc = _normal_bf16(n_cache, key + [10]).view(shape)
@@ -288,12 +300,14 @@ def config_shapes(cfg: int):
     raise ValueError(cfg)
 
 
-def make_config(cfg: int, kind: str, seed: int | None = None, cache_device=None) -> LayerCall:
-    """Workload `cfg` (0..4) for one layer kind ("swa" or "full"); seed defaults to cfg."""
+def make_config(cfg: int, kind: str, seed: int | None = None, cache_device=None,
+                heads=None) -> LayerCall:
+    """Workload `cfg` (0..4) for one layer kind ("swa" or "full"); seed defaults to cfg.
+    heads = (Hq, Hkv) draws the same shapes with other head counts (see make_call)."""
     q_lens, kv_lens, kv_dtype, desc = config_shapes(cfg)
     seed = cfg if seed is None else seed
     call = make_call(q_lens, kv_lens, kind, kv_dtype, [seed, 0 if kind == "swa" else 1],
-                     name=f"config{cfg}-{kind}", cache_device=cache_device)
+                     name=f"config{cfg}-{kind}", cache_device=cache_device, heads=heads)
     call.extra["description"] = desc
     return call
 

@@ -40,7 +40,8 @@ def stage(call, device="cuda"):
     d = {"batch": ba.DeviceBatch(call.q_start, call.kv_len, call.block_table, device),
          "cache": ba.DeviceCache(call.k_cache.to(device), call.v_cache.to(device),
                                  call.k_scale, call.v_scale),
-         "layer": HybridAttention(call.kind)}
+         "layer": HybridAttention(call.kind, num_q_heads=call.num_q_heads,
+                                  num_kv_heads=call.num_kv_heads)}
     for name in ("q", "k", "v", "gate", "q_norm_w", "k_norm_w", "gate_bias"):
         d[name] = getattr(call, name).to(device)
     d["q_out"] = torch.empty_like(d["q"])
