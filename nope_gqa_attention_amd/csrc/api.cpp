@@ -257,7 +257,7 @@ beam_status beam_attn_prefill(const beam_layer_desc* layer, const beam_batch* ba
   if ((s = check_tensor("q", q, q_stride, row, N)) != BEAM_OK) return s;
   if ((s = check_tensor("out", out, out_stride, row, N)) != BEAM_OK) return s;
   if ((s = check_gate(gate, gate_stride, gate_bias, L.Hq, N)) != BEAM_OK) return s;
-  const int64_t tiles = ((int64_t)B.max_q_len * L.G + 255) / 256;
+  const int64_t tiles = ((int64_t)B.max_q_len * L.G + 127) / 128;   // smallest row tile
   if (tiles > 0x7FFFFFFF) return fail(BEAM_ERR_INVALID_ARG, "max_q_len too large");
   return launched(beam::launch_attn_prefill(L, B, C, q, q_stride, gate, gate_stride, gate_bias,
                                             out, out_stride, static_cast<hipStream_t>(stream)));

@@ -9,7 +9,7 @@
 //
 // Design (MFMA-bound, MI355X):
 //  * Rows are (token, query head) pairs of one KV head's group, flattened token-major:
-//    a workgroup owns 256 consecutive rows (about 43 tokens x 6 heads), so every K/V
+//    a workgroup owns 256 (or 128) consecutive rows (about 43 tokens x 6 heads), so every K/V
 //    tile it stages in LDS serves all 6 query heads of the group (GQA reuse) and all of
 //    its tokens. Grid: (row tile, KV head, sequence), remapped so that the row tiles of
 //    one (sequence, KV head) run on one XCD and share its L2.
@@ -19,7 +19,10 @@
 //    Each 256-byte row is stored with its 16-byte chunks XOR-swizzled by the row index so
 //    that the operand reads below hit distinct LDS banks. The block table is read 64
 //    entries at a time, one chunk ahead.
-//  * 8 waves (2 per SIMD) x 32 rows. Per 32-key half of a tile a wave computes
+//  * Full layers: 8 waves (2 per SIMD) x 32 rows = 256 rows per workgroup. Sliding
+//    layers: 4 waves x 32 rows, two workgroups per CU, so that one workgroup's start-up
+//    (Q rows, first tile) and end (output) overlap the other's compute -- a sliding row
+//    tile only spans about 9 key tiles. Per 32-key half of a tile a wave computes
 //    S^T = K Q^T with MFMA 32x32x16 bf16 (K from LDS, Q^T held in registers); a lane
 //    then holds 16 scores of one row, so row max/sum take one cross-half swap
 //    (permlane32).
@@ -41,11 +44,10 @@
 namespace beam {
 namespace {
 
-// Workgroup shape: 8 waves (2 per SIMD) x one 32-row MFMA block = 256 rows.
-constexpr int kRowsPerBlock = 256;
+// Workgroup shape: waves x one 32-row MFMA block each; 8 waves (256 rows) for full
+// layers, 4 (128 rows) for sliding ones. Both keep 2 waves per SIMD (at most 256 VGPRs).
 constexpr int kRowsPerWave = 32;
-constexpr int kWaves = kRowsPerBlock / kRowsPerWave;
-constexpr int kThreads = kWaves * 64;
+constexpr int prefill_waves(int kind) { return kind == BEAM_LAYER_SWA ? 4 : 8; }
 constexpr int kRowBytes = kHeadDim * 2;                  // 256-byte bf16 row, swizzled chunks
 constexpr int kTileBytes = kPage * kRowBytes;            // one K or V page tile: 16 KiB
 constexpr float kLog2e = 1.4426950408889634f;
@@ -53,6 +55,12 @@ constexpr float kRescaleSlack = 8.0f;                    // log2 headroom before
 constexpr int kNumXcds = 8;                              // MI355X: 8 XCDs x 32 CUs
 
 typedef __attribute__((address_space(3))) void lds_void_t;
+// 16-byte direct copy global -> LDS (global_load_lds_dwordx4). A plain function, so that
+// kernel templates whose copy loops depend on template parameters still instantiate in
+// the host compilation pass.
+__device__ __forceinline__ void copy16_to_lds(const void* src, lds_void_t* dst) {
+  __builtin_amdgcn_global_load_lds(src, dst, 16, 0, 0);
+}
 
 // Chunk slot of 16-byte chunk c (0..15) of row r in a swizzled tile: c XOR f(r mod 16),
 // f swapping the two 2-bit halves of r's low nibble. f is a bijection, so the 16 rows a
@@ -100,11 +108,16 @@ __device__ __forceinline__ float swap_halves_sum(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// Launch bound: the larger workgroup (512 threads), which also caps both shapes at 256
+// VGPRs, i.e. 2 waves per SIMD.
 template <int KIND, int KV>
-__global__ __launch_bounds__(kThreads) void prefill_kernel(
+__global__ __launch_bounds__(512) void prefill_kernel(
     LayerParams L, BatchParams B, CacheParams C, const uint16_t* __restrict__ q, int64_t q_stride,
     const uint16_t* __restrict__ gate, int64_t gate_stride, const uint16_t* __restrict__ gate_bias,
     uint16_t* out, int64_t out_stride) {
+  constexpr int kWaves = prefill_waves(KIND);
+  constexpr int kThreads = kWaves * 64;
+  constexpr int kRowsPerBlock = kWaves * kRowsPerWave;
   __shared__ __attribute__((aligned(1024))) unsigned char lds[2 * 2 * kTileBytes];
 
   // Blocks are dispatched round-robin over the 8 XCDs (each with its own L2). Remap the
@@ -199,7 +212,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(
   }
 
   // ---- direct global -> LDS copy of one K and one V page tile. Wave w copies rows
-  // [8w, 8w + 8) of each with 2 instructions per tensor; an instruction moves 64 lanes x
+  // [Rw, Rw + R) of each, R = 64 / waves, with R / 4 instructions per tensor; an instruction moves 64 lanes x
   // 16 bytes = 4 rows into one contiguous 1 KiB block: lane l lands at row 4i + l/16,
   // chunk slot l%16, so it fetches that row's chunk (l%16) ^ swz_key(row).
   constexpr int kRowsCopied = kPage / kWaves;
@@ -222,7 +235,10 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(
   constexpr int kSrcTileBytes = fp8 ? kTileBytes / 2 : kTileBytes;   // one head's page in the cache
   const int64_t head_off = (int64_t)g * kSrcTileBytes;
   const int64_t page_bytes = (int64_t)L.Hkv * kSrcTileBytes;
-  u32x4_t k_stage = {0u, 0u, 0u, 0u}, v_stage = {0u, 0u, 0u, 0u};
+  constexpr int kFp8Reps = kPage * 8 / kThreads;     // fp8 rows staged per thread
+  u32x4_t k_stage[kFp8Reps], v_stage[kFp8Reps];
+#pragma unroll
+  for (int r = 0; r < kFp8Reps; ++r) { k_stage[r] = u32x4_t{0u, 0u, 0u, 0u}; v_stage[r] = k_stage[r]; }
   const int fp8_off = (tid / 8) * kHeadDim + (tid % 8) * 16;   // byte offset in an fp8 page tile
   auto issue_tile = [&](int kt, auto buf_c) {
     constexpr int BUF = decltype(buf_c)::value;
@@ -239,14 +255,18 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(
 #pragma unroll
       for (int i = 0; i < kRowsCopied / 4; ++i) {
         const int dst = BUF * 2 * kTileBytes + (kRowsCopied * wave + 4 * i) * kRowBytes;
-        __builtin_amdgcn_global_load_lds(kb + cp_off[i], (lds_void_t*)(lds + dst), 16, 0, 0);
-        __builtin_amdgcn_global_load_lds(vb + cp_off[i], (lds_void_t*)(lds + dst + kTileBytes), 16, 0, 0);
+        copy16_to_lds(kb + cp_off[i], (lds_void_t*)(lds + dst));
+        copy16_to_lds(vb + cp_off[i], (lds_void_t*)(lds + dst + kTileBytes));
       }
     } else {
-      // thread tid loads 16 codes (bytes 16 * (tid % 8) ..) of fp8 row tid / 8 of each
-      // tensor into registers; store_staged converts and writes them after this tile
-      k_stage = *reinterpret_cast<const u32x4_t*>(kb + fp8_off);
-      v_stage = *reinterpret_cast<const u32x4_t*>(vb + fp8_off);
+      // thread tid loads 16 codes (bytes 16 * (tid % 8) ..) of fp8 rows tid / 8 (+ the
+      // thread count / 8) of each tensor into registers; store_staged converts and
+      // writes them after this tile
+#pragma unroll
+      for (int r = 0; r < kFp8Reps; ++r) {
+        k_stage[r] = *reinterpret_cast<const u32x4_t*>(kb + fp8_off + r * (kThreads / 8) * kHeadDim);
+        v_stage[r] = *reinterpret_cast<const u32x4_t*>(vb + fp8_off + r * (kThreads / 8) * kHeadDim);
+      }
     }
   };
   // fp8: the staged codes of the next tile, converted to bf16, into LDS buffer BUF at the
@@ -255,13 +275,16 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(
     if constexpr (fp8) {
       constexpr int BUF = decltype(buf_c)::value;
       unsigned char* kt_lds = lds + BUF * 2 * kTileBytes;
-      const int row = tid / 8, j = tid % 8;
-      const int s0 = row * kRowBytes + (((2 * j) ^ swz_key(row)) << 4);
-      const int s1 = row * kRowBytes + (((2 * j + 1) ^ swz_key(row)) << 4);
-      *reinterpret_cast<bf16x8_t*>(kt_lds + s0) = fp8x8_to_bf16x8(k_stage[0], k_stage[1]);
-      *reinterpret_cast<bf16x8_t*>(kt_lds + s1) = fp8x8_to_bf16x8(k_stage[2], k_stage[3]);
-      *reinterpret_cast<bf16x8_t*>(kt_lds + kTileBytes + s0) = fp8x8_to_bf16x8(v_stage[0], v_stage[1]);
-      *reinterpret_cast<bf16x8_t*>(kt_lds + kTileBytes + s1) = fp8x8_to_bf16x8(v_stage[2], v_stage[3]);
+#pragma unroll
+      for (int r = 0; r < kFp8Reps; ++r) {
+        const int row = tid / 8 + r * (kThreads / 8), j = tid % 8;
+        const int s0 = row * kRowBytes + (((2 * j) ^ swz_key(row)) << 4);
+        const int s1 = row * kRowBytes + (((2 * j + 1) ^ swz_key(row)) << 4);
+        *reinterpret_cast<bf16x8_t*>(kt_lds + s0) = fp8x8_to_bf16x8(k_stage[r][0], k_stage[r][1]);
+        *reinterpret_cast<bf16x8_t*>(kt_lds + s1) = fp8x8_to_bf16x8(k_stage[r][2], k_stage[r][3]);
+        *reinterpret_cast<bf16x8_t*>(kt_lds + kTileBytes + s0) = fp8x8_to_bf16x8(v_stage[r][0], v_stage[r][1]);
+        *reinterpret_cast<bf16x8_t*>(kt_lds + kTileBytes + s1) = fp8x8_to_bf16x8(v_stage[r][2], v_stage[r][3]);
+      }
     }
   };
 
@@ -452,8 +475,10 @@ hipError_t launch_attn_prefill(const LayerParams& L, const BatchParams& B, const
                                int64_t gate_stride, const void* gate_bias, void* out,
                                int64_t out_stride, hipStream_t stream) {
   if (B.num_tokens == 0 || B.num_seqs == 0 || B.max_q_len == 0) return hipSuccess;
-  const int64_t tiles = ((int64_t)B.max_q_len * L.G + kRowsPerBlock - 1) / kRowsPerBlock;
-  const dim3 grid((unsigned)tiles, (unsigned)L.Hkv, (unsigned)B.num_seqs), block(kThreads);
+  const int rows_per_block = prefill_waves(L.kind) * kRowsPerWave;
+  const int64_t tiles = ((int64_t)B.max_q_len * L.G + rows_per_block - 1) / rows_per_block;
+  const dim3 grid((unsigned)tiles, (unsigned)L.Hkv, (unsigned)B.num_seqs),
+      block(prefill_waves(L.kind) * 64);
   auto launch = [&](auto kernel) {
     hipLaunchKernelGGL(kernel, grid, block, 0, stream, L, B, C, static_cast<const uint16_t*>(q),
                        q_stride, static_cast<const uint16_t*>(gate), gate_stride,
