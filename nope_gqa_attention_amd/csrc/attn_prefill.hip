@@ -418,25 +418,31 @@ __global__ __launch_bounds__(512) void prefill_kernel(
     __syncthreads();                   // ... and everyone's; this buffer is free again
     buf ^= 1;
   };
-  auto masked_step = [&](int kt) {
+  auto masked_step = [&](int kt, auto tail_c) {
     advance(kt);
     const int k0 = kt * kPage;
     const bool skip = !wave_active || k0 > w_max_pos || k0 + kPage - 1 < w_min_lo;
-    if (!skip) compute(k0, buf, std::true_type{}, std::true_type{});
+    if (!skip) compute(k0, buf, std::true_type{}, tail_c);
     finish(kt);
   };
 
+  // Only the sequence's last tile can hold slots past its end (whose V may be anything);
+  // it runs last, on its own, with the V masking. Plain tiles lie wholly before the
+  // first new token, so the tail tile is never one of them.
+  const bool tail_tile = kt_end * kPage > kv;
+  const int kt_stop = tail_tile ? kt_end - 1 : kt_end;
   issue_tile(kt_begin, std::integral_constant<int, 0>{});
   store_staged(std::integral_constant<int, 0>{});
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-  for (int kt = kt_begin; kt < plain_begin; ++kt) masked_step(kt);
+  for (int kt = kt_begin; kt < min(plain_begin, kt_stop); ++kt) masked_step(kt, std::false_type{});
   for (int kt = plain_begin; kt < plain_end; ++kt) {
     advance(kt);
     compute(kt * kPage, buf, std::false_type{}, std::false_type{});
     finish(kt);
   }
-  for (int kt = plain_end; kt < kt_end; ++kt) masked_step(kt);
+  for (int kt = plain_end; kt < kt_stop; ++kt) masked_step(kt, std::false_type{});
+  if (tail_tile) masked_step(kt_end - 1, std::true_type{});
 
   // ---- epilogue: 1/l, gate, bf16 store (lane owns row lr; d values
   // 32*db + 8*(v/4) + 4*half + (v%4))
