@@ -94,6 +94,31 @@ def summarize_counters(paths):
     return "\n".join(lines)
 
 
+def summarize_trace(path):
+    """Markdown table of a rocprofv3 --kernel-trace CSV (`*_kernel_trace.csv`): per
+    libbeamattn kernel and launch shape (workgroups in x, y, z; threads per workgroup),
+    the number of dispatches and their mean / min / max duration in microseconds."""
+    import collections
+    import csv
+    import re
+
+    groups = collections.defaultdict(list)
+    for r in csv.DictReader(open(path)):
+        name = r["Kernel_Name"]
+        if "beam::" not in name:
+            continue
+        short = re.sub(r"\(.*", "", name.replace("(anonymous namespace)::", "").replace("void ", ""))
+        wg = int(r["Workgroup_Size_X"])
+        grid = (int(r["Grid_Size_X"]) // wg, int(r["Grid_Size_Y"]), int(r["Grid_Size_Z"]))
+        groups[(short, grid, wg)].append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    lines = ["| kernel | workgroups (x, y, z) | threads | calls | average us | min us | max us |",
+             "|---|---|---|---|---|---|---|"]
+    for (k, grid, wg), d in sorted(groups.items(), key=lambda kv: -sum(kv[1])):
+        lines.append(f"| {k} | {grid} | {wg} | {len(d)} | {sum(d) / len(d):.2f} | {min(d):.2f} | "
+                     f"{max(d):.2f} |")
+    return "\n".join(lines)
+
+
 def recorded_traffic():
     """HBM bytes per launch of the full-layer prefill kernel from the committed counter
     summary, or None when that summary is missing or was taken on another version of the
@@ -381,12 +406,17 @@ def main():
     ap.add_argument("--summarize-counters", nargs="+", metavar="CSV",
                     help="print the markdown summary of rocprofv3 FETCH_SIZE / WRITE_SIZE counter "
                          "CSVs (no GPU work)")
+    ap.add_argument("--summarize-trace", metavar="CSV",
+                    help="print the markdown summary of a rocprofv3 kernel-trace CSV (no GPU work)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one plain 1 GiB device-to-device copy, whose FETCH_SIZE / "
                          "WRITE_SIZE counters calibrate the traffic of the other kernels")
     args = ap.parse_args()
     if args.summarize_counters:
         print(summarize_counters(args.summarize_counters))
+        return
+    if args.summarize_trace:
+        print(summarize_trace(args.summarize_trace))
         return
     if args.gpus != 1:
         print(f"bench.py runs on exactly one GPU; --gpus {args.gpus} is not supported "
