@@ -336,6 +336,31 @@ def run_decode(args, result):
 
 
 
+def run_prefill_fp8(args, result):
+    """Chunked prefill over an fp8 KV cache: the long-prefill shapes (8 x 2048 new tokens
+    on 98,304 cached) with the cache in fp8 e4m3, both layer kinds (fused store, then
+    prefill attention with the codes widened to bf16 on their way into LDS)."""
+    import torch
+
+    import synth
+
+    res = {}
+    for kind in ("full", "swa"):
+        call = synth.make_config(1, kind, cache_device="cuda", kv_dtype="fp8")
+        s = Staged(call)
+        ql = [int(x) for x in call.q_lens]
+        kl = [int(x) for x in call.kv_len]
+        _, per = timed_steps([("kvwrite", s.kvwrite), ("attn", lambda s=s: s.attend("prefill"))],
+                             args.steps, args.warmup)
+        tf = 4 * D * HQ * visible_pairs(ql, kl, kind) / (per["attn"] * 1e-3) / 1e12
+        res[kind] = {"prefill_ms": round(per["attn"], 4), "kvwrite_ms": round(per["kvwrite"], 4),
+                     "prefill_tflops": round(tf, 1), "prefill_mfma_frac": round(tf / PEAK_BF16_TFLOPS, 4)}
+        log(f"  fp8-cache prefill {kind}: {res[kind]}")
+        del s, call
+        torch.cuda.empty_cache()
+    result["prefill_fp8_cache"] = res
+
+
 def run_head_share(args, result):
     """The share of one of 8 GPUs that split the heads (1 KV head, 6 query heads, its own
     pages): the long prefill (full and SWA layers) and the batch-1 decode and 1M-key verify
@@ -513,6 +538,7 @@ def main():
 
     if not args.no_decode and args.only == "all":  # "--only prefill" skips the decode workloads
         run_decode(args, result)
+        run_prefill_fp8(args, result)
         run_head_share(args, result)
     if args.only in ("all", "prefill"):
         run_projections(args, result, new_tokens)

@@ -301,10 +301,12 @@ def config_shapes(cfg: int):
 
 
 def make_config(cfg: int, kind: str, seed: int | None = None, cache_device=None,
-                heads=None) -> LayerCall:
+                heads=None, kv_dtype: str | None = None) -> LayerCall:
     """Workload `cfg` (0..4) for one layer kind ("swa" or "full"); seed defaults to cfg.
-    heads = (Hq, Hkv) draws the same shapes with other head counts (see make_call)."""
-    q_lens, kv_lens, kv_dtype, desc = config_shapes(cfg)
+    heads = (Hq, Hkv) draws the same shapes with other head counts (see make_call);
+    kv_dtype ("bf16" / "fp8") replaces the workload's cache dtype."""
+    q_lens, kv_lens, cfg_dtype, desc = config_shapes(cfg)
+    kv_dtype = cfg_dtype if kv_dtype is None else kv_dtype
     seed = cfg if seed is None else seed
     call = make_call(q_lens, kv_lens, kind, kv_dtype, [seed, 0 if kind == "swa" else 1],
                      name=f"config{cfg}-{kind}", cache_device=cache_device, heads=heads)

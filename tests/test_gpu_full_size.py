@@ -5,6 +5,7 @@ cache draw, page permutation and NaN-poisoned unused slots), run through the C A
 compared with the fp64 oracle on sampled rows: the oracle reads the very pages the GPU
 read (copied back per sequence), so every sampled output is checked at full context.
   long prefill   8 sequences x 2048 new tokens on 98,304 cached (bf16): 5 rows per sequence
+  the same prefill over an fp8 cache (chunked prefill on fp8 KV): 5 rows per sequence
   batch-1 decode 1 token at p = 100,000 (bf16): the row
   batched decode 32 sequences, 8K..128K keys (fp8): every row
   1M verify      8 tokens on 1,048,576 cached (fp8): every row
@@ -27,8 +28,8 @@ def _lib(gpu_lib):
     yield
 
 
-def _check(cfg, kind, mode, rows_of_seq):
-    call = synth.make_config(cfg, kind, cache_device="cuda")
+def _check(cfg, kind, mode, rows_of_seq, kv_dtype=None):
+    call = synth.make_config(cfg, kind, cache_device="cuda", kv_dtype=kv_dtype)
     say(f"case full-size config{cfg} kind={kind} mode={mode}: {call.num_seqs} seqs, "
         f"{call.num_tokens} tokens, {call.k_cache.shape[0]} pages, {call.kv_dtype}")
     s = Staged(call)
@@ -57,6 +58,11 @@ def _check(cfg, kind, mode, rows_of_seq):
 @pytest.mark.parametrize("kind", ["swa", "full"])
 def test_long_prefill_full_size_sampled_rows(kind):
     _check(1, kind, "prefill", lambda b, n: [0, 63, 64, 1000 + 37 * b, n - 1])
+
+
+@pytest.mark.parametrize("kind", ["swa", "full"])
+def test_long_prefill_fp8_cache_full_size_sampled_rows(kind):
+    _check(1, kind, "prefill", lambda b, n: [0, 63, 64, 1000 + 37 * b, n - 1], kv_dtype="fp8")
 
 
 @pytest.mark.parametrize("kind", ["swa", "full"])
