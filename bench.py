@@ -119,6 +119,40 @@ def summarize_trace(path):
     return "\n".join(lines)
 
 
+def summarize_mfma(paths):
+    """Markdown summary of rocprofv3 --pmc runs with the derived counters MfmaUtil and
+    MfmaFlopsBF16 and the raw GRBM_GUI_ACTIVE (one pass each): per libbeamattn kernel and
+    launch size, the bf16 MFMA FLOPs the hardware counted per dispatch, the rate they give
+    over the dispatch's duration (against the 2.5 PFLOP/s bf16 peak), the MFMA-busy share of
+    SIMD cycles, and the engine clock (GRBM_GUI_ACTIVE is summed over the 8 XCDs)."""
+    import collections
+    import csv
+    import re
+
+    per = collections.defaultdict(lambda: collections.defaultdict(list))
+    for path in paths:
+        for r in csv.DictReader(open(path)):
+            name = r["Kernel_Name"]
+            if "beam::" not in name:
+                continue
+            short = re.sub(r"\(.*", "", name.replace("(anonymous namespace)::", "").replace("void ", ""))
+            key = (short, int(r["Grid_Size"]) // int(r["Workgroup_Size"]))
+            per[key][r["Counter_Name"]].append(float(r["Counter_Value"]))
+            per[key]["dur_" + r["Counter_Name"]].append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-9)
+    mean = lambda v: sum(v) / len(v) if v else None
+    lines = ["| kernel | workgroups | dispatches | MFMA FLOP per dispatch (counted) | counted TFLOP/s | "
+             "share of 2.5 PFLOP/s | MfmaUtil % | clock GHz |", "|---|---|---|---|---|---|---|---|"]
+    for (k, wgs), c in sorted(per.items(), key=lambda kv: -(mean(kv[1].get("MfmaFlopsBF16", [])) or 0)):
+        fl, util, gui = mean(c.get("MfmaFlopsBF16", [])), mean(c.get("MfmaUtil", [])), mean(c.get("GRBM_GUI_ACTIVE", []))
+        tf = fl / mean(c["dur_MfmaFlopsBF16"]) / 1e12 if fl else None
+        clk = gui / 8 / mean(c["dur_GRBM_GUI_ACTIVE"]) / 1e9 if gui else None
+        n = max(len(v) for name, v in c.items() if not name.startswith("dur_"))
+        fmt = lambda v, d: "" if v is None else f"{v:.{d}f}"
+        lines.append(f"| {k} | {wgs} | {n} | {fmt(fl, 0)} | {fmt(tf, 1)} | "
+                     f"{fmt(tf / PEAK_BF16_TFLOPS if tf else None, 4)} | {fmt(util, 1)} | {fmt(clk, 3)} |")
+    return "\n".join(lines)
+
+
 def recorded_traffic():
     """HBM bytes per launch of the full-layer prefill kernel from the committed counter
     summary, or None when that summary is missing or was taken on another version of the
@@ -431,6 +465,9 @@ def main():
     ap.add_argument("--summarize-counters", nargs="+", metavar="CSV",
                     help="print the markdown summary of rocprofv3 FETCH_SIZE / WRITE_SIZE counter "
                          "CSVs (no GPU work)")
+    ap.add_argument("--summarize-mfma", nargs="+", metavar="CSV",
+                    help="print the markdown summary of rocprofv3 MfmaUtil / MfmaFlopsBF16 / "
+                         "GRBM_GUI_ACTIVE counter CSVs (no GPU work)")
     ap.add_argument("--summarize-trace", metavar="CSV",
                     help="print the markdown summary of a rocprofv3 kernel-trace CSV (no GPU work)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -442,6 +479,9 @@ def main():
         return
     if args.summarize_trace:
         print(summarize_trace(args.summarize_trace))
+        return
+    if args.summarize_mfma:
+        print(summarize_mfma(args.summarize_mfma))
         return
     if args.gpus != 1:
         print(f"bench.py runs on exactly one GPU; --gpus {args.gpus} is not supported "
