@@ -48,9 +48,10 @@ def file_sha256(path):
 
 def summarize_counters(paths):
     """Markdown summary of rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE counter CSVs of a bench
-    run with --copy-calibration: per libbeamattn kernel, the mean KiB per dispatch of each
-    counter and the HBM bytes they stand for once scaled by what the same counter read for
-    the plain 1 GiB copy. Ends with the record the bench line's roofline.traffic is read
+    run with --copy-calibration: per libbeamattn kernel and launch size, the mean KiB per
+    dispatch of each counter, the HBM bytes they stand for once scaled by what the same
+    counter read for the plain 1 GiB copy, and the rate those bytes give over the
+    dispatch's own duration. Ends with the record the bench line's roofline.traffic is read
     from, tagged with the hash of the prefill kernel source it was measured on."""
     import collections
     import csv
@@ -66,23 +67,28 @@ def summarize_counters(paths):
             elif "beam::" in name:
                 short = re.sub(r"\(.*", "", name.replace("(anonymous namespace)::", ""))
                 short = short.replace("void ", "")
-                per[short][ctr].append(val)
+                key = (short, int(r["Grid_Size"]) // int(r["Workgroup_Size"]))
+                per[key][ctr].append(val)
+                per[key]["dur_" + ctr].append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-9)
     factor = {c: CALIBRATION_BYTES / 1024 / v for c, v in calib.items() if v > 0}
-    lines = ["| kernel | dispatches | FETCH_SIZE KiB | WRITE_SIZE KiB | HBM GB per dispatch |",
-             "|---|---|---|---|---|"]
+    lines = ["| kernel | workgroups | dispatches | FETCH_SIZE KiB | WRITE_SIZE KiB | HBM GB per dispatch | "
+             "HBM GB/s over the dispatch |", "|---|---|---|---|---|---|---|"]
     record = None
-    for k in sorted(per):
-        f = per[k].get("FETCH_SIZE", [])
-        w = per[k].get("WRITE_SIZE", [])
-        fm = sum(f) / len(f) if f else None
-        wm = sum(w) / len(w) if w else None
-        gb = None
+    mean = lambda v: sum(v) / len(v) if v else None
+    for (k, wgs) in sorted(per):
+        c = per[(k, wgs)]
+        fm, wm = mean(c.get("FETCH_SIZE", [])), mean(c.get("WRITE_SIZE", []))
+        gb = gbs = None
         if fm is not None and wm is not None and factor.get("FETCH_SIZE") and factor.get("WRITE_SIZE"):
-            gb = (fm * factor["FETCH_SIZE"] + wm * factor["WRITE_SIZE"]) * 1024 / 1e9
-        lines.append(f"| {k} | {max(len(f), len(w))} | {fm if fm is None else round(fm, 1)} | "
-                     f"{wm if wm is None else round(wm, 1)} | {gb if gb is None else round(gb, 3)} |")
+            fb, wb = fm * factor["FETCH_SIZE"] * 1024, wm * factor["WRITE_SIZE"] * 1024
+            gb = (fb + wb) / 1e9
+            gbs = fb / mean(c["dur_FETCH_SIZE"]) / 1e9 + wb / mean(c["dur_WRITE_SIZE"]) / 1e9
+        n = max(len(c.get("FETCH_SIZE", [])), len(c.get("WRITE_SIZE", [])))
+        lines.append(f"| {k} | {wgs} | {n} | {fm if fm is None else round(fm, 1)} | "
+                     f"{wm if wm is None else round(wm, 1)} | {gb if gb is None else round(gb, 3)} | "
+                     f"{gbs if gbs is None else round(gbs, 1)} |")
         # the full NoPE layer over a bf16 cache: prefill_kernel<BEAM_LAYER_FULL, BEAM_KV_BF16>
-        if re.search(r"prefill_kernel<1(, 0)?>$", k) and gb is not None:
+        if re.search(r"prefill_kernel<1(, 0)?>$", k) and gb is not None and record is None:
             record = round(gb * 1e9)
     lines.append("")
     lines.append(f"calibration (1 GiB copy): FETCH_SIZE {calib.get('FETCH_SIZE')} KiB -> factor "
