@@ -27,6 +27,11 @@
  *    precondition and is not read by the host: it must satisfy the beam_batch rules
  *    below. No C++ exception crosses this interface, and the library never prints or
  *    aborts.
+ *  - Debug builds (compiled with BEAMATTN_DEBUG, built as libbeamattn_debug.so): the
+ *    K/V-write, prefill and decode entry points first check the device metadata against
+ *    the beam_batch rules on the GPU and return BEAM_ERR_INVALID_ARG naming the first
+ *    broken rule and sequence, before any other kernel runs. That check allocates 4
+ *    bytes and synchronises the stream, so debug builds are not for graph capture.
  */
 #ifndef BEAMATTN_H
 #define BEAMATTN_H
@@ -95,15 +100,15 @@ typedef struct beam_kv_cache {
  * writes use one contract): token pos of sequence b lives in physical page
  * block_table[b * max_pages + pos / page_size] at slot pos % page_size.
  * Preconditions on the device arrays: q_start is non-decreasing with q_start[0] = 0 and
- * q_start[num_seqs] <= num_tokens; n_b <= max_q_len; n_b <= kv_len[b] <= max_kv_len.
+ * q_start[num_seqs] <= num_tokens; n_b <= max_q_len; n_b <= kv_len[b] <= max_kv_len; and
+ * every block_table entry for a page that holds a visible key (and, for the K/V write,
+ * a new token) is in [0, num_pages). Entries for pages with no visible key are never
+ * read.
  * Rows q_start[num_seqs] .. num_tokens-1 are padding: no K/V is stored for them and no
  * attention output is written for them (beam_head_gate, which has no batch, gates them
  * like any row). With padding and host bounds that cover every step (max_q_len,
  * max_kv_len, max_pages), one recorded HIP graph of a decode step replays for any
  * lengths within the bounds: only the device arrays and tensor contents change.
- * every block_table entry for a page that holds a visible key (and, for the K/V write,
- * a new token) is in [0, num_pages). Entries for pages with no visible key are never
- * read.
  * Window-only pools for sliding layers ("Reflection Beam 1.0 on vLLM": sliding layers
  * keep only the window's KV): several logical pages of a sequence may share one
  * physical page, e.g. a ring of R pages with logical page p at ring page p mod R. The

@@ -17,6 +17,9 @@ import torch
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libbeamattn.so")
+# the same library built with BEAMATTN_DEBUG: the K/V-write, prefill and decode entry
+# points also check the device-side batch metadata (synchronously) before launching
+DEBUG_LIB_PATH = os.path.join(HERE, "libbeamattn_debug.so")
 
 BEAM_ABI_VERSION = 2
 BEAM_OK, BEAM_ERR_INVALID_ARG, BEAM_ERR_UNSUPPORTED, BEAM_ERR_WORKSPACE, BEAM_ERR_HIP = range(5)

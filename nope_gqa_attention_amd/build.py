@@ -21,8 +21,10 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(HERE, "_build")
 LIB_PATH = os.path.join(HERE, "libbeamattn.so")
+DEBUG_BUILD_DIR = os.path.join(HERE, "_build_debug")
+DEBUG_LIB_PATH = os.path.join(HERE, "libbeamattn_debug.so")
 SOURCES = ["api.cpp", "qknorm_kvwrite.hip", "head_gate.hip", "attn_decode.hip", "attn_prefill.hip",
-           "linear.hip"]
+           "linear.hip", "validate.hip"]
 ARCH = "gfx950"
 
 
@@ -48,25 +50,27 @@ def _run(cmd, verbose):
     return r
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every source and link libbeamattn.so; returns the library path."""
-    os.makedirs(BUILD_DIR, exist_ok=True)
+def build(verbose: bool = False, debug: bool = False) -> str:
+    """Compile every source and link libbeamattn.so (debug: libbeamattn_debug.so, built
+    with BEAMATTN_DEBUG, whose entry points also check the batch metadata on the GPU);
+    returns the library path."""
+    build_dir, lib_path = (DEBUG_BUILD_DIR, DEBUG_LIB_PATH) if debug else (BUILD_DIR, LIB_PATH)
+    os.makedirs(build_dir, exist_ok=True)
     cc = hipcc()
-    objs = []
+    extra = ["-DBEAMATTN_DEBUG"] if debug else []
 
     def compile_one(src):
-        obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
-        lang = ["-x", "hip"] if src.endswith(".hip") else ["-x", "hip"]
-        _run([cc, *common_flags(), *lang, "-c", os.path.join(CSRC, src), "-o", obj], verbose)
+        obj = os.path.join(build_dir, os.path.splitext(src)[0] + ".o")
+        _run([cc, *common_flags(), *extra, "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj], verbose)
         return obj
 
     with ThreadPoolExecutor(min(8, len(SOURCES))) as ex:
         objs = list(ex.map(compile_one, SOURCES))
-    tmp = LIB_PATH + ".tmp"
+    tmp = lib_path + ".tmp"
     _run([cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs], verbose)
-    os.replace(tmp, LIB_PATH)
-    return LIB_PATH
+    os.replace(tmp, lib_path)
+    return lib_path
 
 
 if __name__ == "__main__":
-    print(build(verbose="-v" in sys.argv))
+    print(build(verbose="-v" in sys.argv, debug="--debug" in sys.argv))

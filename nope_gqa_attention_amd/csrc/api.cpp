@@ -1,6 +1,7 @@
 // C ABI of libbeamattn: validates every host-visible argument, then launches the HIP
 // kernels on the caller's stream. No allocation, no synchronisation, no global mutable
-// state except the thread-local last-error message.
+// state except the thread-local last-error message (debug builds add a synchronous
+// check of the device-resident batch metadata, see debug_check_batch).
 #include <hip/hip_runtime.h>
 
 #include <cmath>
@@ -145,6 +146,8 @@ beam_status check_batch(const beam_batch* B, beam::BatchParams* out) {
   if (B->num_tokens > 0x7FFFFFFF) return fail(BEAM_ERR_INVALID_ARG, "num_tokens too large");
   if (B->max_q_len > B->max_kv_len)
     return fail(BEAM_ERR_INVALID_ARG, "max_q_len exceeds max_kv_len");
+  if (B->max_kv_len > 0x7FFFFFFF)
+    return fail(BEAM_ERR_INVALID_ARG, "max_kv_len must fit in int32 (kv_len entries are int32)");
   if ((int64_t)B->max_pages * beam::kPage < B->max_kv_len)
     return fail(BEAM_ERR_INVALID_ARG, "max_pages (%d) * 64 < max_kv_len (%lld)", B->max_pages,
                 (long long)B->max_kv_len);
@@ -195,6 +198,43 @@ beam_status launched(hipError_t e) {
   return ok();
 }
 
+#ifdef BEAMATTN_DEBUG
+// Debug builds only: check the device-resident batch metadata against the beam_batch
+// rules before any kernel reads it. Allocates a 4-byte result, synchronises the stream
+// and frees it, so it is neither allocation-free nor usable under graph capture.
+beam_status debug_check_batch(const beam::LayerParams& L, const beam::BatchParams& B,
+                              int64_t num_pages, hipStream_t stream) {
+  if (B.num_seqs == 0) return BEAM_OK;
+  int* err = nullptr;
+  if (hipMalloc(&err, sizeof(int)) != hipSuccess)
+    return fail(BEAM_ERR_HIP, "batch check: hipMalloc failed");
+  int h = 0;
+  hipError_t e = hipMemsetAsync(err, 0, sizeof(int), stream);
+  if (e == hipSuccess) e = beam::launch_validate_batch(L, B, num_pages, err, stream);
+  if (e == hipSuccess) e = hipMemcpyAsync(&h, err, sizeof(int), hipMemcpyDeviceToHost, stream);
+  if (e == hipSuccess) e = hipStreamSynchronize(stream);
+  hipFree(err);
+  if (e != hipSuccess) return fail(BEAM_ERR_HIP, "batch check: %s", hipGetErrorString(e));
+  if (h == 0) return BEAM_OK;
+  static const char* const what[] = {
+      "", "q_start[0] is not 0", "q_start decreases", "q_start[num_seqs] exceeds num_tokens",
+      "new tokens exceed max_q_len", "kv_len is below the sequence's new tokens",
+      "kv_len exceeds max_kv_len", "a block_table entry the call reads is outside [0, num_pages)"};
+  const int code = h / 65536, seq = h % 65536;
+  return fail(BEAM_ERR_INVALID_ARG, "batch metadata: %s (sequence %d)",
+              code >= 1 && code <= 7 ? what[code] : "unknown rule", seq);
+}
+#define BEAM_DEBUG_CHECK_BATCH(L, B, C, stream)                                                  \
+  do {                                                                                          \
+    beam_status ds_ = debug_check_batch(L, B, (C).num_pages, static_cast<hipStream_t>(stream)); \
+    if (ds_ != BEAM_OK) return ds_;                                                             \
+  } while (0)
+#else
+#define BEAM_DEBUG_CHECK_BATCH(L, B, C, stream) \
+  do {                                          \
+  } while (0)
+#endif
+
 bool ranges_overlap(const void* a, int64_t a_bytes, const void* b, int64_t b_bytes) {
   const uintptr_t pa = reinterpret_cast<uintptr_t>(a), pb = reinterpret_cast<uintptr_t>(b);
   return pa < pb + (uintptr_t)b_bytes && pb < pa + (uintptr_t)a_bytes;
@@ -236,6 +276,7 @@ beam_status beam_qknorm_rope_ssmax_kvwrite(const beam_layer_desc* layer, const b
       return fail(BEAM_ERR_INVALID_ARG, "in-place q_out needs q_out_stride == q_stride");
     }
   }
+  BEAM_DEBUG_CHECK_BATCH(L, B, C, stream);
   return launched(beam::launch_qknorm_kvwrite(L, B, C, q, q_stride, k, k_stride, v, v_stride,
                                               q_norm_w, k_norm_w, norm_w_head_stride, q_out,
                                               q_out_stride, static_cast<hipStream_t>(stream)));
@@ -257,8 +298,9 @@ beam_status beam_attn_prefill(const beam_layer_desc* layer, const beam_batch* ba
   if ((s = check_tensor("q", q, q_stride, row, N)) != BEAM_OK) return s;
   if ((s = check_tensor("out", out, out_stride, row, N)) != BEAM_OK) return s;
   if ((s = check_gate(gate, gate_stride, gate_bias, L.Hq, N)) != BEAM_OK) return s;
-  const int64_t tiles = ((int64_t)B.max_q_len * L.G + 127) / 128;   // smallest row tile
-  if (tiles > 0x7FFFFFFF) return fail(BEAM_ERR_INVALID_ARG, "max_q_len too large");
+  if ((int64_t)B.max_q_len * L.G > 0x7FFFFFFF)
+    return fail(BEAM_ERR_INVALID_ARG, "max_q_len * query heads per KV head must fit in int32");
+  BEAM_DEBUG_CHECK_BATCH(L, B, C, stream);
   return launched(beam::launch_attn_prefill(L, B, C, q, q_stride, gate, gate_stride, gate_bias,
                                             out, out_stride, static_cast<hipStream_t>(stream)));
 }
@@ -302,6 +344,7 @@ beam_status beam_attn_decode(const beam_layer_desc* layer, const beam_batch* bat
     if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
       return fail(BEAM_ERR_INVALID_ARG, "decode workspace must be 256-byte aligned");
   }
+  BEAM_DEBUG_CHECK_BATCH(L, B, C, stream);
   return launched(beam::launch_attn_decode(L, B, C, S, q, q_stride, gate, gate_stride, gate_bias,
                                            out, out_stride, workspace,
                                            static_cast<hipStream_t>(stream)));

@@ -68,6 +68,20 @@ hipError_t launch_linear_bf16(int64_t M, int64_t N, int64_t K, const void* x, in
                               const void* w, int64_t w_stride, void* y, int64_t y_stride,
                               hipStream_t stream);
 
+// Batch-metadata check (BEAMATTN_DEBUG builds): *err (device, zeroed by the caller) gets
+// code * 65536 + sequence of the first rule found broken, or stays 0.
+enum BatchError {
+  kBadQStart0 = 1,    // q_start[0] != 0
+  kBadQOrder = 2,     // q_start decreases
+  kBadTokens = 3,     // q_start[num_seqs] > num_tokens
+  kBadQLen = 4,       // n_b > max_q_len
+  kBadKvShort = 5,    // kv_len[b] < n_b
+  kBadKvLong = 6,     // kv_len[b] > max_kv_len
+  kBadPage = 7,       // a block-table entry the call touches is outside [0, num_pages)
+};
+hipError_t launch_validate_batch(const LayerParams& L, const BatchParams& B, int64_t num_pages,
+                                 int* err, hipStream_t stream);
+
 hipError_t launch_head_gate(const LayerParams& L, int64_t num_tokens, const void* attn,
                             int64_t attn_stride, const void* gate, int64_t gate_stride,
                             const void* gate_bias, void* out, int64_t out_stride,

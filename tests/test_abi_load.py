@@ -11,6 +11,7 @@ import pytest
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "beamattn.h")
 LIB = os.path.join(ROOT, "nope_gqa_attention_amd", "libbeamattn.so")
+DEBUG_LIB = os.path.join(ROOT, "nope_gqa_attention_amd", "libbeamattn_debug.so")
 
 
 def declared_functions():
@@ -36,6 +37,17 @@ def test_header_declares_the_four_entry_points():
 
 def test_library_exports_every_declared_symbol(lib):
     missing = [n for n in declared_functions() if not hasattr(lib, n)]
+    assert not missing, missing
+
+
+def test_debug_library_loads_and_exports_every_declared_symbol():
+    """The BEAMATTN_DEBUG build (device-side batch-metadata checks) is built beside the
+    library and exports the same interface."""
+    if not os.path.exists(DEBUG_LIB):
+        pytest.fail("libbeamattn_debug.so is not built (python -m nope_gqa_attention_amd.build --debug)")
+    import torch  # noqa: F401
+    dbg = ctypes.CDLL(DEBUG_LIB)
+    missing = [n for n in declared_functions() if not hasattr(dbg, n)]
     assert not missing, missing
 
 
