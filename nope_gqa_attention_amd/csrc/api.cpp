@@ -91,6 +91,9 @@ beam::DecodeSplit choose_decode_split(int32_t G, int32_t kind, int32_t window, i
     kps = ((kps + step - 1) / step) * step;
     if (kps < min_keys) kps = min_keys;
   }
+  // the merge kernel holds one weight per split in LDS
+  const int64_t kps_cap = (range + beam::kDecodeMaxSplits - 1) / beam::kDecodeMaxSplits;
+  if (kps < kps_cap) kps = ((kps_cap + step - 1) / step) * step;
   s.keys_per_split = (int32_t)kps;
   s.num_splits = (int32_t)((range + kps - 1) / kps);
   if (s.num_splits < 1) s.num_splits = 1;

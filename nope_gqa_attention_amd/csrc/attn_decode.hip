@@ -38,6 +38,8 @@ constexpr int kVRowsPerWave = 32;                 // keys staged per half-page s
 constexpr int kLdsBytes = kDecodeWaves * kVRowsPerWave * kVRowBytes;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kRescaleSlack = 8.0f;                // log2 headroom before rescaling
+constexpr int kBufferRsrcWord3 = 0x00020000;         // raw buffer, 32-bit data format (CDNA)
+constexpr int kLoadNonTemporal = 2;                  // cache-policy bit: nt
 
 // Start of the 8-value slice of head dimension used by MFMA i (0..3) in lane group g
 // (lane / 16). bf16: one 16-byte load per MFMA; fp8: one 16-byte load feeds 2 MFMAs.
@@ -183,20 +185,38 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(decode
     for (int it = 0; it < 4; ++it) voff[it] = (lane / 8 + 8 * it) * kRow + (lane % 8) * 16;
   }
   const int64_t head_bytes = (int64_t)kPage * kRow;       // one KV head's page
-  auto fetch = [&](int j, u32x4_t* kr, u32x4_t* vr) {
-    const int pi = j >> 1, hs = j & 1;
-    const int64_t page = page_of(pi);
-    const int64_t base = (page * L.Hkv + g) * head_bytes + (int64_t)(32 * hs) * kRow;
-    const char* kb = static_cast<const char*>(C.k) + base;
-    const char* vb = static_cast<const char*>(C.v) + base;
-#pragma unroll
-    for (int i = 0; i < kKRegs; ++i) kr[i] = *reinterpret_cast<const u32x4_t*>(kb + koff[i]);
-#pragma unroll
-    for (int i = 0; i < kVRegs; ++i) vr[i] = *reinterpret_cast<const u32x4_t*>(vb + voff[i]);
+  // One buffer resource per half-page: the uniform base sits in scalar registers and
+  // each lane adds a 32-bit offset, so no per-lane 64-bit addresses are formed. The
+  // loads carry the non-temporal hint: every cache byte is read once per call, and
+  // streaming it past the caches raised the achieved HBM rate by about 10%.
+  auto page_base = [&](int j) -> int64_t {
+    const int64_t page = page_of(j >> 1);
+    return (page * L.Hkv + g) * head_bytes + (int64_t)(32 * (j & 1)) * kRow;
   };
+  auto half_rsrc = [&](const void* p, int j) {
+    return __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<char*>(static_cast<const char*>(p) + page_base(j)), 0, 32 * kRow, kBufferRsrcWord3);
+  };
+  auto fetch_k = [&](int j) {
+    const __amdgpu_buffer_rsrc_t r = half_rsrc(C.k, j);
+#pragma unroll
+    for (int i = 0; i < kKRegs; ++i) kreg[i] = __builtin_amdgcn_raw_buffer_load_b128(r, koff[i], 0, kLoadNonTemporal);
+  };
+  auto fetch_v = [&](int j) {
+    const __amdgpu_buffer_rsrc_t r = half_rsrc(C.v, j);
+#pragma unroll
+    for (int i = 0; i < kVRegs; ++i) vreg[i] = __builtin_amdgcn_raw_buffer_load_b128(r, voff[i], 0, kLoadNonTemporal);
+  };
+  // With two or three 16-row blocks (2 waves per SIMD) the loop is software-pipelined
+  // in the one register set: the next half-step's K loads are issued as soon as the
+  // score MFMAs have read this step's K, and its V loads once V is staged in LDS, so
+  // they fly during the softmax and P V (-11% time on the 8-token 1M-key verify). With
+  // one block, 3 resident waves per SIMD hide the latency better than the pipeline,
+  // whose live registers would cost that residency. bf16 with three blocks has no
+  // registers to spare for it.
+  constexpr bool kPipe = RB >= 2 && !(KV == BEAM_KV_BF16 && RB == 3);
 
-
-  auto compute = [&](const u32x4_t* kreg, const u32x4_t* vreg, int j) {
+  auto compute = [&](int j) {
     const int kk0 = (int)(first_pk + (int64_t)kDecodeKeysPerBlockStep * (j >> 1) + 32 * (j & 1));
     // ---- S^T = K Q^T (32 keys = 2 score blocks of 16)
     f32x4_t sc[RB][2];
@@ -222,6 +242,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(decode
         sc[rb][sb] = sacc;
       }
     }
+    if (kPipe && j + 1 < n_half) fetch_k(j + 1);
     // ---- stage V rows (row-major bf16) in this wave's LDS region; keys >= kv are
     // zeroed so that their (zero) probabilities never meet NaN payloads
     if (KV == BEAM_KV_BF16) {
@@ -243,6 +264,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(decode
         *reinterpret_cast<bf16x8_t*>(vlds + r * kVRowBytes + cc * 32 + 16) = fp8x8_to_bf16x8(w[2], w[3]);
       }
     }
+    if (kPipe && j + 1 < n_half) fetch_v(j + 1);
     // ---- mask, online softmax, P^T as bf16 (k-slot order: block 0 keys 4lg..4lg+3,
     // then block 1 keys 16+4lg..)
     const bool need_mask = (kk0 + 31 > all_hi) || (kk0 < all_lo);
@@ -311,11 +333,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(decode
     }
   };
 
-  // one register set: fetch a half-step, compute it; other waves hide the latency
+  if (kPipe) {
+    if (n_half > 0) { fetch_k(0); fetch_v(0); }
 #pragma unroll 1
-  for (int j = 0; j < n_half; ++j) {
-    fetch(j, kreg, vreg);
-    compute(kreg, vreg, j);
+    for (int j = 0; j < n_half; ++j) compute(j);
+  } else {
+    // one register set: fetch a half-step, compute it; other waves hide the latency
+#pragma unroll 1
+    for (int j = 0; j < n_half; ++j) { fetch_k(j); fetch_v(j); compute(j); }
   }
 
   // ---- merge the 4 waves of this workgroup (LDS), then write
@@ -391,21 +416,28 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(decode
 }
 
 // Log-sum-exp merge of the split partials of each (token, head) row, then the gate.
-// One 256-thread workgroup per row: the 4 waves take splits w, w+4, ... with independent
-// loads in flight, each lane owning 2 of the 128 output dims; the waves then combine in
-// a fixed order through LDS.
-__global__ __launch_bounds__(256) void decode_merge_kernel(
+// One 256-thread workgroup per row. Lane group (t % 32) owns 4 of the 128 output dims
+// and split group t / 32 the splits t/32, t/32 + 8, ...; the (m, l) pairs and the first
+// 128 splits' partial outputs are all requested before anything waits, so the merge
+// costs one memory round trip. Sums run in a fixed order (bitwise reproducible).
+constexpr int kMergeThreads = 256;
+constexpr int kMergeGroups = kMergeThreads / 32;       // split groups
+constexpr int kMergeUnroll = 16;                        // partials in flight per thread
+constexpr int kMergeChunk = kMergeGroups * kMergeUnroll;
+
+__global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(
     LayerParams L, BatchParams B, DecodeSplit S, const float* __restrict__ ws_o,
     const float* __restrict__ ws_ml, int64_t ws_rows, const uint16_t* __restrict__ gate,
     int64_t gate_stride, const uint16_t* __restrict__ gate_bias, uint16_t* out,
     int64_t out_stride) {
-  __shared__ float s_red[4];
-  __shared__ float s_o[4][kHeadDim];
-  __shared__ float s_l[4];
+  __shared__ float s_w[kDecodeMaxSplits];
+  __shared__ float s_red[kMergeThreads / 64];
+  __shared__ f32x4_t s_acc[kMergeGroups][32];
   const int64_t row = blockIdx.x;                 // tok * Hq + h
   const int64_t tok = row / L.Hq;
   const int h = (int)(row % L.Hq);
-  const int wave = threadIdx.x / 64, lane = threadIdx.x % 64;
+  const int t = threadIdx.x, wave = t / 64, lane = t % 64;
+  const int q4 = t % 32, grp = t / 32;
   if (tok >= B.q_start[B.num_seqs]) return;      // padding row past the last sequence
   const int b = seq_of_token(B.q_start, B.num_seqs, tok);
   const int64_t n = (int64_t)B.q_start[b + 1] - B.q_start[b];
@@ -413,43 +445,75 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(
   const int64_t base = range_base(L, kv, n);
   const int used = (int)((kv - base + S.keys_per_split - 1) / S.keys_per_split);
 
-  float M = -INFINITY;
-  for (int s = threadIdx.x; s < used; s += 256) M = fmaxf(M, ws_ml[((int64_t)s * ws_rows + row) * 2]);
-  for (int o = 32; o >= 1; o >>= 1) M = fmaxf(M, __shfl_xor(M, o, 64));
+  // ---- issue: this thread's first (m, l) pair and its first chunk of partial outputs
+  float2 ml0 = make_float2(-INFINITY, 0.f);
+  if (t < used) ml0 = *reinterpret_cast<const float2*>(ws_ml + ((int64_t)t * ws_rows + row) * 2);
+  f32x4_t ov[kMergeUnroll];
+#pragma unroll
+  for (int u = 0; u < kMergeUnroll; ++u) {
+    const int sp = grp + kMergeGroups * u;
+    ov[u] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    if (sp < used) ov[u] = *reinterpret_cast<const f32x4_t*>(ws_o + ((int64_t)sp * ws_rows + row) * kHeadDim + 4 * q4);
+  }
+  // ---- global max of the split maxima
+  float M = ml0.x;
+  for (int sp = t + kMergeThreads; sp < used; sp += kMergeThreads)
+    M = fmaxf(M, ws_ml[((int64_t)sp * ws_rows + row) * 2]);
+  M = wave_xor_max(M, 1); M = wave_xor_max(M, 2); M = wave_xor_max(M, 4);
+  M = wave_xor_max(M, 8); M = wave_xor_max(M, 16); M = wave_xor_max(M, 32);
   if (lane == 0) s_red[wave] = M;
   __syncthreads();
   M = fmaxf(fmaxf(s_red[0], s_red[1]), fmaxf(s_red[2], s_red[3]));
-
-  float lsum = 0.f, o0 = 0.f, o1 = 0.f;
-#pragma unroll 4
-  for (int s = wave; s < used; s += 4) {
-    const int64_t wrow = (int64_t)s * ws_rows + row;
-    const float2 ml = *reinterpret_cast<const float2*>(ws_ml + wrow * 2);
-    const float2 o = *reinterpret_cast<const float2*>(ws_o + wrow * kHeadDim + 2 * lane);
+  __syncthreads();                                 // s_red is reused for the sum below
+  // ---- split weights (LDS) and the weighted sum of the l's
+  float lsum = 0.f;
+  for (int sp = t; sp < used; sp += kMergeThreads) {
+    const float2 ml = sp == t ? ml0 : *reinterpret_cast<const float2*>(ws_ml + ((int64_t)sp * ws_rows + row) * 2);
     const float w = ml.x == -INFINITY ? 0.f : exp2f(ml.x - M);
+    s_w[sp] = w;
     lsum += w * ml.y;
-    o0 += w * o.x;
-    o1 += w * o.y;
   }
-  s_o[wave][2 * lane] = o0;
-  s_o[wave][2 * lane + 1] = o1;
-  if (lane == 0) s_l[wave] = lsum;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) lsum += __shfl_xor(lsum, o, 64);
+  if (lane == 0) s_red[wave] = lsum;
   __syncthreads();
-  if (wave != 0) return;
-  const float ltot = ((s_l[0] + s_l[1]) + s_l[2]) + s_l[3];
-  const int d = 2 * lane;
-  float y0 = ((s_o[0][d] + s_o[1][d]) + s_o[2][d]) + s_o[3][d];
-  float y1 = ((s_o[0][d + 1] + s_o[1][d + 1]) + s_o[2][d + 1]) + s_o[3][d + 1];
-  const float inv = ltot > 0.f ? 1.0f / ltot : 0.f;
-  y0 *= inv;
-  y1 *= inv;
-  if (gate != nullptr) {
-    const uint32_t gw = *reinterpret_cast<const uint32_t*>(gate + tok * gate_stride + (int64_t)h * kHeadDim + d);
-    const float bh = bf16_to_f32(gate_bias[h]);
-    y0 *= 1.0f / (1.0f + expf(-(bf16_to_f32(gw & 0xFFFFu) + bh)));
-    y1 *= 1.0f / (1.0f + expf(-(bf16_to_f32(gw >> 16) + bh)));
+  const float ltot = ((s_red[0] + s_red[1]) + s_red[2]) + s_red[3];
+  // ---- weighted partial outputs, chunk by chunk
+  f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+  for (int c0 = 0; c0 < used; c0 += kMergeChunk) {
+    if (c0 > 0) {
+#pragma unroll
+      for (int u = 0; u < kMergeUnroll; ++u) {
+        const int sp = c0 + grp + kMergeGroups * u;
+        ov[u] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        if (sp < used) ov[u] = *reinterpret_cast<const f32x4_t*>(ws_o + ((int64_t)sp * ws_rows + row) * kHeadDim + 4 * q4);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kMergeUnroll; ++u) {
+      const int sp = c0 + grp + kMergeGroups * u;
+      if (sp < used) acc += s_w[sp] * ov[u];
+    }
   }
-  *reinterpret_cast<uint32_t*>(out + tok * out_stride + (int64_t)h * kHeadDim + d) = pack_bf16x2(y0, y1);
+  s_acc[grp][q4] = acc;
+  __syncthreads();
+  if (t >= 32) return;
+  f32x4_t y = s_acc[0][q4];
+#pragma unroll
+  for (int gi = 1; gi < kMergeGroups; ++gi) y += s_acc[gi][q4];
+  const float inv = ltot > 0.f ? 1.0f / ltot : 0.f;
+  y *= inv;
+  const int d = 4 * q4;
+  if (gate != nullptr) {
+    const u32x2_t gw = *reinterpret_cast<const u32x2_t*>(gate + tok * gate_stride + (int64_t)h * kHeadDim + d);
+    const float bh = bf16_to_f32(gate_bias[h]);
+    y[0] *= 1.0f / (1.0f + expf(-(bf16_to_f32(gw[0] & 0xFFFFu) + bh)));
+    y[1] *= 1.0f / (1.0f + expf(-(bf16_to_f32(gw[0] >> 16) + bh)));
+    y[2] *= 1.0f / (1.0f + expf(-(bf16_to_f32(gw[1] & 0xFFFFu) + bh)));
+    y[3] *= 1.0f / (1.0f + expf(-(bf16_to_f32(gw[1] >> 16) + bh)));
+  }
+  const u32x2_t packed = {pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3])};
+  *reinterpret_cast<u32x2_t*>(out + tok * out_stride + (int64_t)h * kHeadDim + d) = packed;
 }
 
 template <int KV>
@@ -474,7 +538,7 @@ hipError_t launch_kv(const LayerParams& L, const BatchParams& B, const CachePara
 #undef BEAM_DECODE_LAUNCH
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || S.num_splits == 1) return e;
-  hipLaunchKernelGGL(decode_merge_kernel, dim3((unsigned)(B.num_tokens * L.Hq)), dim3(256), 0, stream, L,
+  hipLaunchKernelGGL(decode_merge_kernel, dim3((unsigned)(B.num_tokens * L.Hq)), dim3(kMergeThreads), 0, stream, L,
                      B, S, ws_o, ws_ml, ws_rows, static_cast<const uint16_t*>(gate), gate_stride,
                      static_cast<const uint16_t*>(gate_bias), static_cast<uint16_t*>(out),
                      out_stride);

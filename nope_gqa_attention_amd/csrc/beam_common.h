@@ -53,6 +53,7 @@ struct DecodeSplit {
 constexpr int kDecodeWaves = 4;                       // waves per decode workgroup
 constexpr int kDecodeKeysPerBlockStep = kDecodeWaves * kPage;  // one page per wave per step
 constexpr int kDecodeMaxRowsPerChunk = 48;
+constexpr int kDecodeMaxSplits = 2048;                // bound of the merge kernel's weight table
 // Decode split-kernel workgroups resident per CU that its register budget is built for
 // (waves per SIMD): 3 with one 16-row block, 2 with two or three. LDS (36 KiB per
 // workgroup) admits 4.
