@@ -354,36 +354,44 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(decode
     }
   }
   __syncthreads();                     // every wave is done with its V region
-  // Sum the waves' outputs in a fixed order (wave 0 writes, waves 1..3 add in turn) so
-  // results are bitwise reproducible; [48 rows][128] fp32 fits in the V regions.
-  float* o_sum = reinterpret_cast<float*>(lds);
-  for (int w = 0; w < kDecodeWaves; ++w) {
-    if (wave == w) {
+  // The waves' outputs, each scaled to the workgroup's row maximum, go into kRegions
+  // fp32 [rows][128] regions of the V staging space (padded rows; one 16-byte write per
+  // accumulator). Waves w and w + kRegions share region w: the first writes, the later
+  // ones add in turn, so sums run in a fixed order (bitwise reproducible).
+  constexpr int kORow = kHeadDim * 4 + 16;                        // padded fp32 row
+  constexpr int kRegions = kLdsBytes / (RB * 16 * kORow) >= kDecodeWaves ? kDecodeWaves
+                           : kLdsBytes / (RB * 16 * kORow) >= 2 ? 2 : 1;
+  static_assert(kLdsBytes >= RB * 16 * kORow, "one output region must fit the staging space");
+  float wgt[RB];
 #pragma unroll
-      for (int rb = 0; rb < RB; ++rb) {
-        const int row = 16 * rb + lc;
-        float mw = -INFINITY;
+  for (int rb = 0; rb < RB; ++rb) {
+    const int row = 16 * rb + lc;
+    float mw = -INFINITY;
 #pragma unroll
-        for (int u = 0; u < kDecodeWaves; ++u) mw = fmaxf(mw, s_m[u][row]);
-        const float wgt = (m_run[rb] == -INFINITY) ? 0.f : exp2f(m_run[rb] - mw);
+    for (int u = 0; u < kDecodeWaves; ++u) mw = fmaxf(mw, s_m[u][row]);
+    wgt[rb] = (m_run[rb] == -INFINITY) ? 0.f : exp2f(m_run[rb] - mw);
+  }
 #pragma unroll
-        for (int db = 0; db < 8; ++db)
+  for (int round = 0; round < kDecodeWaves / kRegions; ++round) {
+    if (wave / kRegions == round) {
+      unsigned char* reg = lds + (wave % kRegions) * (RB * 16 * kORow);
 #pragma unroll
-          for (int v = 0; v < 4; ++v) {
-            float* dst = &o_sum[row * kHeadDim + 16 * db + 4 * lg + v];
-            const float val = acc[rb][db][v] * wgt;
-            *dst = (w == 0) ? val : *dst + val;
-          }
-      }
+      for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+        for (int db = 0; db < 8; ++db) {
+          f32x4_t* dst = reinterpret_cast<f32x4_t*>(reg + (16 * rb + lc) * kORow + (16 * db + 4 * lg) * 4);
+          const f32x4_t val = acc[rb][db] * wgt[rb];
+          *dst = round == 0 ? val : *dst + val;
+        }
     }
     __syncthreads();
   }
 
-  // one thread per (row, 2 dims) writes the workgroup's result
+  // one thread per (row, 4 dims) writes the workgroup's result
   const float vsc = (KV == BEAM_KV_FP8_E4M3) ? C.v_scale : 1.0f;
-  for (int i = threadIdx.x; i < S.rows_per_chunk * (kHeadDim / 2); i += kThreads) {
-    const int row = i / (kHeadDim / 2);
-    const int d = 2 * (i % (kHeadDim / 2));
+  for (int i = threadIdx.x; i < S.rows_per_chunk * (kHeadDim / 4); i += kThreads) {
+    const int row = i / (kHeadDim / 4);
+    const int d = 4 * (i % (kHeadDim / 4));
     const int64_t r = row0 + row;
     if (r >= rows_b) continue;
     float mw = -INFINITY;
@@ -396,20 +404,27 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(decode
     const int64_t t = r / L.G;
     const int h = g * L.G + (int)(r % L.G);
     const int64_t tok = q0 + t;
-    const float o0 = o_sum[row * kHeadDim + d] * vsc, o1 = o_sum[row * kHeadDim + d + 1] * vsc;
+    f32x4_t o = *reinterpret_cast<const f32x4_t*>(lds + row * kORow + d * 4);
+#pragma unroll
+    for (int rg = 1; rg < kRegions; ++rg)
+      o += *reinterpret_cast<const f32x4_t*>(lds + rg * (RB * 16 * kORow) + row * kORow + d * 4);
+    o *= vsc;
     if (S.num_splits == 1) {
       const float inv = lw > 0.f ? 1.0f / lw : 0.f;
-      float y0 = o0 * inv, y1 = o1 * inv;
+      f32x4_t y = o * inv;
       if (gate != nullptr) {
-        const uint32_t gw = *reinterpret_cast<const uint32_t*>(gate + tok * gate_stride + (int64_t)h * kHeadDim + d);
+        const u32x2_t gw = *reinterpret_cast<const u32x2_t*>(gate + tok * gate_stride + (int64_t)h * kHeadDim + d);
         const float bh = bf16_to_f32(gate_bias[h]);
-        y0 *= 1.0f / (1.0f + expf(-(bf16_to_f32(gw & 0xFFFFu) + bh)));
-        y1 *= 1.0f / (1.0f + expf(-(bf16_to_f32(gw >> 16) + bh)));
+        y[0] *= 1.0f / (1.0f + expf(-(bf16_to_f32(gw[0] & 0xFFFFu) + bh)));
+        y[1] *= 1.0f / (1.0f + expf(-(bf16_to_f32(gw[0] >> 16) + bh)));
+        y[2] *= 1.0f / (1.0f + expf(-(bf16_to_f32(gw[1] & 0xFFFFu) + bh)));
+        y[3] *= 1.0f / (1.0f + expf(-(bf16_to_f32(gw[1] >> 16) + bh)));
       }
-      *reinterpret_cast<uint32_t*>(out + tok * out_stride + (int64_t)h * kHeadDim + d) = pack_bf16x2(y0, y1);
+      const u32x2_t packed = {pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3])};
+      *reinterpret_cast<u32x2_t*>(out + tok * out_stride + (int64_t)h * kHeadDim + d) = packed;
     } else {
       const int64_t wrow = (int64_t)split * ws_rows + tok * L.Hq + h;
-      *reinterpret_cast<float2*>(ws_o + wrow * kHeadDim + d) = make_float2(o0, o1);
+      *reinterpret_cast<f32x4_t*>(ws_o + wrow * kHeadDim + d) = o;
       if (d == 0) *reinterpret_cast<float2*>(ws_ml + wrow * 2) = make_float2(mw, lw);
     }
   }
