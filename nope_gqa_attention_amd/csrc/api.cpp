@@ -97,6 +97,15 @@ beam::DecodeSplit choose_decode_split(int32_t G, int32_t kind, int32_t window, i
   s.keys_per_split = (int32_t)kps;
   s.num_splits = (int32_t)((range + kps - 1) / kps);
   if (s.num_splits < 1) s.num_splits = 1;
+  // A launch of one split that leaves most CUs idle is latency-bound: there, 16-row
+  // chunks (each reading the same keys) finish sooner than one workgroup that carries
+  // two or three 16-row blocks through every step. Re-read bytes are what this trades,
+  // so it applies only while the workgroups are fewer than the CUs.
+  if (s.num_splits == 1 && s.rows_per_chunk > 16 &&
+      (int64_t)num_seqs * Hkv * s.row_chunks < decode_cu_count()) {
+    s.row_chunks = (int32_t)((rows + 15) / 16);
+    s.rows_per_chunk = 16;
+  }
   return s;
 }
 
