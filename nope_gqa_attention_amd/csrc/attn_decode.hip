@@ -32,10 +32,16 @@
 namespace beam {
 namespace {
 
-constexpr int kThreads = kDecodeWaves * 64;
 constexpr int kVRowBytes = kHeadDim * 2 + 16;     // bf16 V row in LDS, padded
 constexpr int kVRowsPerWave = 32;                 // keys staged per half-page step
-constexpr int kLdsBytes = kDecodeWaves * kVRowsPerWave * kVRowBytes;
+constexpr int lds_bytes(int waves) { return waves * kVRowsPerWave * kVRowBytes; }
+// Output regions of the in-workgroup merge: the largest divisor of the wave count whose
+// regions (fp32 [rows][128], padded) fit the V staging space.
+constexpr int merge_regions(int waves, int region_bytes) {
+  int r = waves;
+  while (r > 1 && (waves % r != 0 || r * region_bytes > lds_bytes(waves))) --r;
+  return r;
+}
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kRescaleSlack = 8.0f;                // log2 headroom before rescaling
 constexpr int kBufferRsrcWord3 = 0x00020000;         // raw buffer, 32-bit data format (CDNA)
@@ -66,15 +72,18 @@ __device__ __forceinline__ int64_t range_base(const LayerParams& L, int64_t kv, 
   return (lo / kPage) * kPage;
 }
 
-template <int KV, int RB>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(decode_wgs_per_cu(RB)))) void decode_split_kernel(
+template <int KV, int RB, int W>
+__global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(decode_wgs_per_cu(RB)))) void decode_split_kernel(
     LayerParams L, BatchParams B, CacheParams C, DecodeSplit S,
     const uint16_t* __restrict__ q, int64_t q_stride, const uint16_t* __restrict__ gate,
     int64_t gate_stride, const uint16_t* __restrict__ gate_bias, uint16_t* out,
     int64_t out_stride, float* __restrict__ ws_o, float* __restrict__ ws_ml, int64_t ws_rows) {
+  constexpr int kThreads = W * 64;
+  constexpr int kLdsBytes = lds_bytes(W);
+  constexpr int kStep = W * kPage;                    // keys of one page per wave
   __shared__ __attribute__((aligned(16))) unsigned char lds[kLdsBytes];
-  __shared__ float s_m[kDecodeWaves][kDecodeMaxRowsPerChunk];
-  __shared__ float s_l[kDecodeWaves][kDecodeMaxRowsPerChunk];
+  __shared__ float s_m[W][kDecodeMaxRowsPerChunk];
+  __shared__ float s_l[W][kDecodeMaxRowsPerChunk];
 
   const int split = blockIdx.x;
   const int g = blockIdx.y / S.row_chunks;
@@ -136,15 +145,15 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(decode
 
   unsigned char* vlds = lds + wave * kVRowsPerWave * kVRowBytes;
 
-  // This wave's pages: keys pk = k_begin + 64*(wave + 4*pi), pi = 0, 1, ...; each page is
+  // This wave's pages: keys pk = k_begin + 64*(wave + W*pi), pi = 0, 1, ...; each page is
   // two half-steps of 32 keys, each loaded into one register set and then computed. The
   // kernel is built for 2-3 resident waves per SIMD, whose loads hide each other's
   // latency; a second register set per wave would halve that residency.
   const int64_t first_pk = k_begin + (int64_t)kPage * wave;
   int n_half = 0;
   if (first_pk < k_end) {
-    const int64_t n_pages = (k_end - first_pk + kDecodeKeysPerBlockStep - 1) / kDecodeKeysPerBlockStep;
-    const int64_t last_pk = first_pk + (n_pages - 1) * kDecodeKeysPerBlockStep;
+    const int64_t n_pages = (k_end - first_pk + kStep - 1) / kStep;
+    const int64_t last_pk = first_pk + (n_pages - 1) * kStep;
     n_half = (int)(2 * (n_pages - 1) + (last_pk + 32 < k_end ? 2 : 1));
   }
   // block-table entries of the wave's pages, 64 at a time: lane i holds page i of the chunk
@@ -154,7 +163,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(decode
   auto page_of = [&](int pi) -> int64_t {
     if (pi / 64 != bt_chunk) {
       bt_chunk = pi / 64;
-      const int64_t my_pk = first_pk + (int64_t)kDecodeKeysPerBlockStep * (64 * bt_chunk + lane);
+      const int64_t my_pk = first_pk + (int64_t)kStep * (64 * bt_chunk + lane);
       bt_lane = my_pk < k_end ? bt_row[my_pk / kPage] : 0;
     }
     return (int64_t)__builtin_amdgcn_readlane(bt_lane, pi % 64);
@@ -217,7 +226,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(decode
   constexpr bool kPipe = RB >= 2 && !(KV == BEAM_KV_BF16 && RB == 3);
 
   auto compute = [&](int j) {
-    const int kk0 = (int)(first_pk + (int64_t)kDecodeKeysPerBlockStep * (j >> 1) + 32 * (j & 1));
+    const int kk0 = (int)(first_pk + (int64_t)kStep * (j >> 1) + 32 * (j & 1));
     // ---- S^T = K Q^T (32 keys = 2 score blocks of 16)
     f32x4_t sc[RB][2];
 #pragma unroll
@@ -343,7 +352,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(decode
     for (int j = 0; j < n_half; ++j) { fetch_k(j); fetch_v(j); compute(j); }
   }
 
-  // ---- merge the 4 waves of this workgroup (LDS), then write
+  // ---- merge the waves of this workgroup (LDS), then write
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) {
     l_run[rb] += __shfl_xor(l_run[rb], 16, 64);
@@ -359,8 +368,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(decode
   // accumulator). Waves w and w + kRegions share region w: the first writes, the later
   // ones add in turn, so sums run in a fixed order (bitwise reproducible).
   constexpr int kORow = kHeadDim * 4 + 16;                        // padded fp32 row
-  constexpr int kRegions = kLdsBytes / (RB * 16 * kORow) >= kDecodeWaves ? kDecodeWaves
-                           : kLdsBytes / (RB * 16 * kORow) >= 2 ? 2 : 1;
+  constexpr int kRegions = merge_regions(W, RB * 16 * kORow);
   static_assert(kLdsBytes >= RB * 16 * kORow, "one output region must fit the staging space");
   float wgt[RB];
 #pragma unroll
@@ -368,11 +376,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(decode
     const int row = 16 * rb + lc;
     float mw = -INFINITY;
 #pragma unroll
-    for (int u = 0; u < kDecodeWaves; ++u) mw = fmaxf(mw, s_m[u][row]);
+    for (int u = 0; u < W; ++u) mw = fmaxf(mw, s_m[u][row]);
     wgt[rb] = (m_run[rb] == -INFINITY) ? 0.f : exp2f(m_run[rb] - mw);
   }
 #pragma unroll
-  for (int round = 0; round < kDecodeWaves / kRegions; ++round) {
+  for (int round = 0; round < W / kRegions; ++round) {
     if (wave / kRegions == round) {
       unsigned char* reg = lds + (wave % kRegions) * (RB * 16 * kORow);
 #pragma unroll
@@ -396,10 +404,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(decode
     if (r >= rows_b) continue;
     float mw = -INFINITY;
 #pragma unroll
-    for (int w = 0; w < kDecodeWaves; ++w) mw = fmaxf(mw, s_m[w][row]);
+    for (int w = 0; w < W; ++w) mw = fmaxf(mw, s_m[w][row]);
     float lw = 0.f;
 #pragma unroll
-    for (int w = 0; w < kDecodeWaves; ++w)
+    for (int w = 0; w < W; ++w)
       lw += (s_m[w][row] == -INFINITY) ? 0.f : s_l[w][row] * exp2f(s_m[w][row] - mw);
     const int64_t t = r / L.G;
     const int h = g * L.G + (int)(r % L.G);
@@ -539,17 +547,18 @@ hipError_t launch_kv(const LayerParams& L, const BatchParams& B, const CachePara
   const int64_t ws_rows = (int64_t)B.num_seqs * B.max_q_len * L.Hq;
   float* ws_o = static_cast<float*>(workspace);
   float* ws_ml = ws_o + (S.num_splits > 1 ? (int64_t)S.num_splits * ws_rows * kHeadDim : 0);
-  const dim3 grid(S.num_splits, L.Hkv * S.row_chunks, B.num_seqs), block(kThreads);
+  const dim3 grid(S.num_splits, L.Hkv * S.row_chunks, B.num_seqs);
   const int rb = S.rows_per_chunk / 16;
-#define BEAM_DECODE_LAUNCH(RBV)                                                               \
-  hipLaunchKernelGGL((decode_split_kernel<KV, RBV>), grid, block, 0, stream, L, B, C, S,      \
-                     static_cast<const uint16_t*>(q), q_stride,                               \
-                     static_cast<const uint16_t*>(gate), gate_stride,                         \
-                     static_cast<const uint16_t*>(gate_bias), static_cast<uint16_t*>(out),    \
+#define BEAM_DECODE_LAUNCH(RBV, WV)                                                            \
+  hipLaunchKernelGGL((decode_split_kernel<KV, RBV, WV>), grid, dim3(WV * 64), 0, stream, L, B, \
+                     C, S, static_cast<const uint16_t*>(q), q_stride,                          \
+                     static_cast<const uint16_t*>(gate), gate_stride,                          \
+                     static_cast<const uint16_t*>(gate_bias), static_cast<uint16_t*>(out),     \
                      out_stride, ws_o, ws_ml, ws_rows)
-  if (rb == 1) BEAM_DECODE_LAUNCH(1);
-  else if (rb == 2) BEAM_DECODE_LAUNCH(2);
-  else BEAM_DECODE_LAUNCH(3);
+  if (rb == 1 && S.waves == kDecodeWideWaves) BEAM_DECODE_LAUNCH(1, kDecodeWideWaves);
+  else if (rb == 1) BEAM_DECODE_LAUNCH(1, kDecodeWaves);
+  else if (rb == 2) BEAM_DECODE_LAUNCH(2, kDecodeWaves);
+  else BEAM_DECODE_LAUNCH(3, kDecodeWaves);
 #undef BEAM_DECODE_LAUNCH
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || S.num_splits == 1) return e;

@@ -48,9 +48,13 @@ struct DecodeSplit {
   int32_t keys_per_split;      // multiple of kDecodeKeysPerBlockStep
   int32_t row_chunks;          // ceil(G * max_q_len / kDecodeRowsPerChunk)
   int32_t rows_per_chunk;      // 16, 32 or 48 (a multiple of 16)
+  int32_t waves;               // waves per workgroup: kDecodeWaves, or kDecodeWideWaves
 };
 
 constexpr int kDecodeWaves = 4;                       // waves per decode workgroup
+// Waves per workgroup of a latency-bound single-split launch (one 16-row block): one
+// workgroup per CU, 3 waves per SIMD, each wave streaming about one page.
+constexpr int kDecodeWideWaves = 12;
 constexpr int kDecodeKeysPerBlockStep = kDecodeWaves * kPage;  // one page per wave per step
 constexpr int kDecodeMaxRowsPerChunk = 48;
 constexpr int kDecodeMaxSplits = 2048;                // bound of the merge kernel's weight table
