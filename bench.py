@@ -356,6 +356,17 @@ def run_decode(args, result):
                 git["i"] += 1
             _, per_g = timed_steps([("step", run_graph)], max(args.steps, 5) * 2, args.warmup)
             del graphs
+            # attention alone, 20 calls back to back in one graph (cache copies alternating):
+            # the device time per call without host launch overhead, which dominates the
+            # eager timing of the latency-bound sliding-window calls
+            n_rep = 20
+            g20 = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g20):
+                for r in range(n_rep):
+                    copies[r % len(copies)].attend("decode")
+            _, per_g20 = timed_steps([("rep", g20.replay)], max(args.steps, 5), args.warmup)
+            del g20
+            dev_ms = per_g20["rep"] / n_rep
             bpk = 2 * HKV * D * (2 if call.kv_dtype == "bf16" else 1)
             nbytes = visible_keys_decode(ql, kl, kind) * bpk
             gbs = nbytes / (per_d["decode"] * 1e-3) / 1e9
@@ -368,6 +379,8 @@ def run_decode(args, result):
                 "tokens_per_s": round(sum(ql) / ((per_d["decode"] + per_d["kvwrite"]) * 1e-3), 1),
                 "step_eager_us": round((per_d["decode"] + per_d["kvwrite"]) * 1e3, 2),
                 "step_graph_us": round(per_g["step"] * 1e3, 2),
+                "decode_graph_us": round(dev_ms * 1e3, 2),
+                "hbm_frac_graph": round(nbytes / (dev_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
             }
             log(f"  decode config{cfg}-{kind}: {dec[f'config{cfg}-{kind}']}")
             del s, copies, call
