@@ -17,8 +17,8 @@
 //    global memory into LDS with gfx950's global_load_lds_dwordx4 (no staging registers)
 //    and double-buffered: the next page is in flight while the current one is consumed.
 //    Each 256-byte row is stored with its 16-byte chunks XOR-swizzled by the row index so
-//    that the operand reads below hit distinct LDS banks. The block table is read 64
-//    entries at a time, one chunk ahead.
+//    that the operand reads below hit distinct LDS banks. Page numbers come from the
+//    block table through scalar loads, one tile ahead.
 //  * Full layers: 8 waves (2 per SIMD) x 32 rows = 256 rows per workgroup. Sliding
 //    layers: 4 waves x 32 rows, two workgroups per CU, so that one workgroup's start-up
 //    (Q rows, first tile) and end (output) overlap the other's compute -- a sliding row
@@ -222,16 +222,12 @@ __global__ __launch_bounds__(512) void prefill_kernel(
     const int row = kRowsCopied * wave + 4 * i + lane / 16;
     cp_off[i] = row * kRowBytes + (((lane % 16) ^ swz_key(row)) << 4);
   }
-  const int32_t* bt_row = B.block_table + (int64_t)b * B.max_pages;
-  // Physical pages of the tiles, 64 per chunk, one entry per lane: chunk c holds tiles
-  // kt_begin + 64c + lane. The next chunk is loaded while the current one is in use, so
-  // the per-tile lookup is a register read, not a memory round trip.
-  auto load_chunk = [&](int c) {
-    const int t = kt_begin + 64 * c + lane;
-    return t < kt_end ? bt_row[t] : 0;
-  };
-  int bt_cur = load_chunk(0);
-  int bt_next = load_chunk(1);
+  // Physical pages come through scalar loads: the block table is read-only for the
+  // kernel's lifetime, so it is read through the constant address space, one scalar
+  // load per tile issued a tile ahead of its use.
+  typedef __attribute__((address_space(4))) const int32_t const_i32_t;
+  const_i32_t* bt_row = (const_i32_t*)(B.block_table + (int64_t)b * B.max_pages);
+  int page_ahead = bt_row[kt_begin];
   constexpr int kSrcTileBytes = fp8 ? kTileBytes / 2 : kTileBytes;   // one head's page in the cache
   const int64_t head_off = (int64_t)g * kSrcTileBytes;
   const int64_t page_bytes = (int64_t)L.Hkv * kSrcTileBytes;
@@ -242,12 +238,9 @@ __global__ __launch_bounds__(512) void prefill_kernel(
   const int fp8_off = (tid / 8) * kHeadDim + (tid % 8) * 16;   // byte offset in an fp8 page tile
   auto issue_tile = [&](int kt, auto buf_c) {
     constexpr int BUF = decltype(buf_c)::value;
-    const int rel = kt - kt_begin;
-    if ((rel & 63) == 0 && rel > 0) {
-      bt_cur = bt_next;
-      bt_next = load_chunk(rel / 64 + 1);
-    }
-    const int page = __builtin_amdgcn_readlane(bt_cur, rel & 63);
+    // page_ahead holds tile kt's page (loaded one issue earlier); fetch the next one
+    const int page = page_ahead;
+    page_ahead = bt_row[kt + 1 < kt_end ? kt + 1 : kt];
     const int64_t base = (int64_t)page * page_bytes + head_off;
     const char* kb = static_cast<const char*>(C.k) + base;
     const char* vb = static_cast<const char*>(C.v) + base;
