@@ -54,7 +54,8 @@ int decode_cu_count() {
 }
 
 beam::DecodeSplit choose_decode_split(int32_t G, int32_t kind, int32_t window, int32_t num_seqs,
-                                      int32_t max_q_len, int64_t max_kv_len, int32_t Hkv) {
+                                      int32_t max_q_len, int64_t max_kv_len, int32_t Hkv,
+                                      int32_t kv_dtype) {
   beam::DecodeSplit s{};
   const int64_t rows = (int64_t)G * max_q_len;
   s.row_chunks = (int32_t)((rows + beam::kDecodeMaxRowsPerChunk - 1) / beam::kDecodeMaxRowsPerChunk);
@@ -69,7 +70,7 @@ beam::DecodeSplit choose_decode_split(int32_t G, int32_t kind, int32_t window, i
   }
   if (range < 1) range = 1;
   const int64_t unit = (int64_t)num_seqs * Hkv * s.row_chunks;   // workgroups per split index
-  const int64_t slots = (int64_t)decode_cu_count() * beam::decode_wgs_per_cu(s.rows_per_chunk / 16);
+  const int64_t slots = (int64_t)decode_cu_count() * beam::decode_wgs_per_cu(s.rows_per_chunk / 16, kv_dtype);
   const int64_t step = beam::kDecodeKeysPerBlockStep;
   const int64_t rows_in_chunk = rows < s.rows_per_chunk ? rows : s.rows_per_chunk;
   int64_t min_keys = rows_in_chunk * (beam::kHeadDim + 2) * 4 * 64 / 256;
@@ -330,9 +331,15 @@ size_t beam_attn_decode_workspace_bytes(const beam_layer_desc* layer, int32_t nu
   beam::LayerParams L;
   if (check_layer(layer, &L) != BEAM_OK) return 0;
   if (num_seqs < 0 || max_q_len < 1 || max_q_len > 16 || max_kv_len < max_q_len) return 0;
-  const beam::DecodeSplit s =
-      choose_decode_split(L.G, L.kind, L.window, num_seqs, max_q_len, max_kv_len, L.Hkv);
-  return decode_workspace_bytes(s, num_seqs, max_q_len, L.Hq);
+  // the split depends on the cache dtype (resident workgroups per CU): size for either
+  size_t need = 0;
+  for (int32_t dt : {(int32_t)BEAM_KV_BF16, (int32_t)BEAM_KV_FP8_E4M3}) {
+    const beam::DecodeSplit s =
+        choose_decode_split(L.G, L.kind, L.window, num_seqs, max_q_len, max_kv_len, L.Hkv, dt);
+    const size_t b = decode_workspace_bytes(s, num_seqs, max_q_len, L.Hq);
+    if (b > need) need = b;
+  }
+  return need;
 }
 
 beam_status beam_attn_decode(const beam_layer_desc* layer, const beam_batch* batch,
@@ -355,7 +362,7 @@ beam_status beam_attn_decode(const beam_layer_desc* layer, const beam_batch* bat
   if ((s = check_tensor("out", out, out_stride, row, N)) != BEAM_OK) return s;
   if ((s = check_gate(gate, gate_stride, gate_bias, L.Hq, N)) != BEAM_OK) return s;
   const beam::DecodeSplit S = choose_decode_split(L.G, L.kind, L.window, B.num_seqs, B.max_q_len,
-                                                  B.max_kv_len, L.Hkv);
+                                                  B.max_kv_len, L.Hkv, C.dtype);
   const size_t need = decode_workspace_bytes(S, B.num_seqs, B.max_q_len, L.Hq);
   if (need > 0) {
     if (!workspace || workspace_bytes < need)

@@ -73,7 +73,7 @@ __device__ __forceinline__ int64_t range_base(const LayerParams& L, int64_t kv, 
 }
 
 template <int KV, int RB, int W>
-__global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(decode_wgs_per_cu(RB)))) void decode_split_kernel(
+__global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(W == kDecodeWideWaves ? 3 : decode_wgs_per_cu(RB, KV)))) void decode_split_kernel(
     LayerParams L, BatchParams B, CacheParams C, DecodeSplit S,
     const uint16_t* __restrict__ q, int64_t q_stride, const uint16_t* __restrict__ gate,
     int64_t gate_stride, const uint16_t* __restrict__ gate_bias, uint16_t* out,
@@ -216,14 +216,16 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(decode_w
 #pragma unroll
     for (int i = 0; i < kVRegs; ++i) vreg[i] = __builtin_amdgcn_raw_buffer_load_b128(r, voff[i], 0, kLoadNonTemporal);
   };
-  // With two or three 16-row blocks (2 waves per SIMD) the loop is software-pipelined
-  // in the one register set: the next half-step's K loads are issued as soon as the
-  // score MFMAs have read this step's K, and its V loads once V is staged in LDS, so
-  // they fly during the softmax and P V (-11% time on the 8-token 1M-key verify). With
-  // one block, 3 resident waves per SIMD hide the latency better than the pipeline,
-  // whose live registers would cost that residency. bf16 with three blocks has no
-  // registers to spare for it.
-  constexpr bool kPipe = RB >= 2 && !(KV == BEAM_KV_BF16 && RB == 3);
+  // With 2 waves per SIMD the loop is software-pipelined inside the one register set: the
+  // next half-step's K loads are issued as soon as the score MFMAs have read this step's
+  // K, and its V loads once V is staged in LDS, so they fly during the softmax and P V
+  // (-11% time on the 8-token 1M-key verify, -7% on batch-1 bf16 decode against the
+  // unpipelined loop at 3 waves per SIMD). One block over an fp8 cache keeps 3 resident
+  // waves and the plain loop (faster there: each half-step is half the bytes); bf16 with
+  // three blocks has no registers to spare; the wide single-split workgroups run at 3
+  // waves per SIMD.
+  constexpr bool kPipe = W == kDecodeWaves && decode_wgs_per_cu(RB, KV) == 2 &&
+                         !(KV == BEAM_KV_BF16 && RB == 3);
 
   auto compute = [&](int j) {
     const int kk0 = (int)(first_pk + (int64_t)kStep * (j >> 1) + 32 * (j & 1));

@@ -58,10 +58,13 @@ constexpr int kDecodeWideWaves = 12;
 constexpr int kDecodeKeysPerBlockStep = kDecodeWaves * kPage;  // one page per wave per step
 constexpr int kDecodeMaxRowsPerChunk = 48;
 constexpr int kDecodeMaxSplits = 2048;                // bound of the merge kernel's weight table
-// Decode split-kernel workgroups resident per CU that its register budget is built for
-// (waves per SIMD): 3 with one 16-row block, 2 with two or three. LDS (36 KiB per
-// workgroup) admits 4.
-constexpr int decode_wgs_per_cu(int row_blocks) { return row_blocks == 1 ? 3 : 2; }
+// Decode split-kernel workgroups (of 4 waves) resident per CU that its register budget is
+// built for, i.e. waves per SIMD: 3 for one 16-row block over an fp8 cache (loads hidden by
+// residency), 2 otherwise (bf16 with one block streams with its next loads in flight,
+// which needs the registers of the third wave). LDS (36 KiB per workgroup) admits 4.
+constexpr int decode_wgs_per_cu(int row_blocks, int kv_dtype) {
+  return (row_blocks == 1 && kv_dtype == BEAM_KV_FP8_E4M3) ? 3 : 2;
+}
 
 hipError_t launch_qknorm_kvwrite(const LayerParams& L, const BatchParams& B, const CacheParams& C,
                                  const void* q, int64_t q_stride, const void* k, int64_t k_stride,
