@@ -13,8 +13,10 @@
 //  * Grid (split, KV head x row chunk, sequence). A row is one (new token, query head)
 //    pair of the KV head's group: G*n_b rows, up to 48 per chunk, all sharing every K/V
 //    byte that is read, so each byte of the cache crosses HBM once per layer call.
-//  * A workgroup is 4 waves; wave w streams pages w, w+4, ... of its split: a 64-key
-//    page of one KV head is one contiguous 16 KiB (bf16) / 8 KiB (fp8) block.
+//  * A workgroup is W waves (4; 12 for latency-bound single-split launches); wave w
+//    streams pages w, w+W, ... of its split: a 64-key page of one KV head is one
+//    contiguous 16 KiB (bf16) / 8 KiB (fp8) block, read in 32-key halves through
+//    non-temporal buffer loads.
 //  * Scores use MFMA 16x16x32 bf16 as S^T = K Q^T: K comes straight from global memory
 //    as the A operand (fp8 codes decoded to bf16 exactly in registers; the scale folds
 //    into the softmax scale), Q^T stays in registers. Each lane then owns one row's
@@ -24,9 +26,9 @@
 //    LDS read (ds_read_b64_tr_b16), so no register transpose is needed.
 //  * The running max is raised only when a row's maximum grows by more than 2^8 (log2
 //    domain), so the output rescale is skipped on almost every step.
-//  * The 4 waves merge their (max, sum, output) in LDS; splits are merged by
-//    log-sum-exp in a second kernel, which also applies the gate; with one split the
-//    first kernel writes the gated output itself.
+//  * The waves merge their (max, sum, output) in LDS; splits are merged by log-sum-exp
+//    in a second kernel, which also applies the gate; with one split the first kernel
+//    writes the gated output itself.
 #include "beam_common.h"
 
 namespace beam {
