@@ -465,23 +465,30 @@ __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(
   const int h = (int)(row % L.Hq);
   const int t = threadIdx.x, wave = t / 64, lane = t % 64;
   const int q4 = t % 32, grp = t / 32;
+  // ---- issue first, before the batch metadata arrives: this row's gate values, this
+  // thread's first (m, l) pair and its first chunk of partial outputs, for every split the
+  // launch has (the workspace holds them all; splits this row's sequence did not use are
+  // read but never weighed)
+  u32x2_t gw = {0u, 0u};
+  if (gate != nullptr && t < 32) gw = *reinterpret_cast<const u32x2_t*>(gate + tok * gate_stride + (int64_t)h * kHeadDim + 4 * q4);
+  // (rows past the workspace's are padding rows: they read nothing and return below)
+  const int nsp = row < ws_rows ? S.num_splits : 0;
+  float2 ml0 = make_float2(-INFINITY, 0.f);
+  if (t < nsp) ml0 = *reinterpret_cast<const float2*>(ws_ml + ((int64_t)t * ws_rows + row) * 2);
+  f32x4_t ov[kMergeUnroll];
+#pragma unroll
+  for (int u = 0; u < kMergeUnroll; ++u) {
+    const int sp = grp + kMergeGroups * u;
+    ov[u] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    if (sp < nsp) ov[u] = *reinterpret_cast<const f32x4_t*>(ws_o + ((int64_t)sp * ws_rows + row) * kHeadDim + 4 * q4);
+  }
   if (tok >= B.q_start[B.num_seqs]) return;      // padding row past the last sequence
   const int b = seq_of_token(B.q_start, B.num_seqs, tok);
   const int64_t n = (int64_t)B.q_start[b + 1] - B.q_start[b];
   const int64_t kv = B.kv_len[b];
   const int64_t base = range_base(L, kv, n);
   const int used = (int)((kv - base + S.keys_per_split - 1) / S.keys_per_split);
-
-  // ---- issue: this thread's first (m, l) pair and its first chunk of partial outputs
-  float2 ml0 = make_float2(-INFINITY, 0.f);
-  if (t < used) ml0 = *reinterpret_cast<const float2*>(ws_ml + ((int64_t)t * ws_rows + row) * 2);
-  f32x4_t ov[kMergeUnroll];
-#pragma unroll
-  for (int u = 0; u < kMergeUnroll; ++u) {
-    const int sp = grp + kMergeGroups * u;
-    ov[u] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    if (sp < used) ov[u] = *reinterpret_cast<const f32x4_t*>(ws_o + ((int64_t)sp * ws_rows + row) * kHeadDim + 4 * q4);
-  }
+  if (t >= used) ml0 = make_float2(-INFINITY, 0.f);
   // ---- global max of the split maxima
   float M = ml0.x;
   for (int sp = t + kMergeThreads; sp < used; sp += kMergeThreads)
@@ -532,7 +539,6 @@ __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(
   y *= inv;
   const int d = 4 * q4;
   if (gate != nullptr) {
-    const u32x2_t gw = *reinterpret_cast<const u32x2_t*>(gate + tok * gate_stride + (int64_t)h * kHeadDim + d);
     const float bh = bf16_to_f32(gate_bias[h]);
     y[0] *= 1.0f / (1.0f + expf(-(bf16_to_f32(gw[0] & 0xFFFFu) + bh)));
     y[1] *= 1.0f / (1.0f + expf(-(bf16_to_f32(gw[0] >> 16) + bh)));
