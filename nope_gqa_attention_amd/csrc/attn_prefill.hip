@@ -73,7 +73,7 @@ __device__ __forceinline__ int swz(int r, int c) { return r * kRowBytes + ((c ^ 
 __device__ __forceinline__ float swap_halves_max(float x) {
   const uint32_t u = __float_as_uint(x);
   const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  return __builtin_elementwise_maximum(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 template <typename F, int... I>
 __device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
@@ -334,9 +334,9 @@ __global__ __launch_bounds__(512) void prefill_kernel(
           if (j > row_pos || j < row_lo) sc[v] = -INFINITY;
         }
       }
-      float mx = __builtin_fmaxf(__builtin_fmaxf(sc[0], sc[1]), sc[2]);
+      float mx = __builtin_elementwise_maximum(__builtin_elementwise_maximum(sc[0], sc[1]), sc[2]);
 #pragma unroll
-      for (int v = 3; v < 16; v += 2) mx = __builtin_fmaxf(__builtin_fmaxf(mx, sc[v]), sc[v + 1 < 16 ? v + 1 : v]);
+      for (int v = 3; v < 16; v += 2) mx = __builtin_elementwise_maximum(__builtin_elementwise_maximum(mx, sc[v]), sc[v + 1 < 16 ? v + 1 : v]);
       mx = swap_halves_max(mx) * c;
       // raise the running max only when it grew by more than the slack
       if (__builtin_amdgcn_ballot_w64(mx > m_run + kRescaleSlack) != 0) {
