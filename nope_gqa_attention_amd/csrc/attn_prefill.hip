@@ -187,6 +187,11 @@ __global__ __launch_bounds__(512) void prefill_kernel(
   constexpr bool fp8 = KV == BEAM_KV_FP8_E4M3;
   const float c = L.sm_scale * kLog2e * (fp8 ? C.k_scale : 1.0f);
   float m_run = -INFINITY, l_run = 0.f;
+  // Loop-carried forms of the running max, so that the common half tile spends no
+  // instruction on them: the exponent offset (0 while the row has seen no key) and the
+  // rescale threshold in raw-score units (c > 0: the entry point rejects other scales).
+  const float inv_c = 1.0f / c;
+  float neg_m = 0.f, thr_raw = -INFINITY;
   f32x16_t acc[4];
 #pragma unroll
   for (int db = 0; db < 4; ++db)
@@ -337,25 +342,26 @@ __global__ __launch_bounds__(512) void prefill_kernel(
       float mx = __builtin_elementwise_maximum(__builtin_elementwise_maximum(sc[0], sc[1]), sc[2]);
 #pragma unroll
       for (int v = 3; v < 16; v += 2) mx = __builtin_elementwise_maximum(__builtin_elementwise_maximum(mx, sc[v]), sc[v + 1 < 16 ? v + 1 : v]);
-      mx = swap_halves_max(mx) * c;
+      mx = swap_halves_max(mx);
       // raise the running max only when it grew by more than the slack
-      if (__builtin_amdgcn_ballot_w64(mx > m_run + kRescaleSlack) != 0) {
-        const float m_new = fmaxf(m_run, mx);
+      if (__builtin_amdgcn_ballot_w64(mx > thr_raw) != 0) {
+        const float m_new = fmaxf(m_run, mx * c);
         // 0 when this row saw no key before; 1 when it still sees none
         const float alpha = m_new == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
         l_run *= alpha;
 #pragma unroll
         for (int db = 0; db < 4; ++db) acc[db] *= alpha;
         m_run = m_new;
+        neg_m = m_new == -INFINITY ? 0.f : -m_new;
+        thr_raw = (m_new + kRescaleSlack) * inv_c;
       }
-      const float m_use = m_run == -INFINITY ? 0.f : m_run;
       bf16x8_t pop[2];
-      float psum = 0.f;
+      float psum = -0.f;                   // -0 + p folds to p
 #pragma unroll
       for (int cc = 0; cc < 2; ++cc) {
 #pragma unroll
         for (int jj = 0; jj < 8; ++jj) {
-          const float p = __builtin_amdgcn_exp2f(fmaf(sc[8 * cc + jj], c, -m_use));
+          const float p = __builtin_amdgcn_exp2f(fmaf(sc[8 * cc + jj], c, neg_m));
           psum += p;
           pop[cc][jj] = (__bf16)p;
         }
