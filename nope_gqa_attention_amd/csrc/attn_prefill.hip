@@ -75,6 +75,9 @@ __device__ __forceinline__ float swap_halves_max(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
   return __builtin_elementwise_maximum(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
+// BUF of a std::integral_constant<int, BUF> argument, -1 for a run-time int
+template <typename T> struct const_buf { static constexpr int value = -1; };
+template <int N> struct const_buf<std::integral_constant<int, N>> { static constexpr int value = N; };
 template <typename F, int... I>
 __device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
   (f(std::integral_constant<int, I>{}), ...);
@@ -288,10 +291,14 @@ __global__ __launch_bounds__(512) void prefill_kernel(
 
   // ---- one 64-key tile from LDS buffer BUF: MASK when some key is invisible to some row
   // of the wave, TAIL when the tile holds slots past the sequence end (NaN allowed there)
-  auto compute = [&](int k0, int buf, auto mask_c, auto tail_c) {
+  auto compute = [&](int k0, auto buf_v, auto mask_c, auto tail_c) {
     constexpr bool MASK = decltype(mask_c)::value;
     constexpr bool TAIL = decltype(tail_c)::value;
-    const unsigned char* tl = lds + buf * 2 * kTileBytes;      // this tile's K; V follows
+    // a compile-time buffer index puts the buffer offset into the LDS reads' immediates
+    constexpr int CB = const_buf<decltype(buf_v)>::value;
+    const int buf = CB >= 0 ? 0 : (int)buf_v;
+    constexpr int kImm = CB >= 0 ? CB * 2 * kTileBytes : 0;
+    const unsigned char* tl = lds + kImm + buf * 2 * kTileBytes;   // this tile's K; V follows
     // per-lane LDS byte addresses of this tile's V operand rows (halves and 16-key steps
     // are immediate offsets on top)
     const uint32_t vbase = lds_addr + buf * 2 * kTileBytes + kTileBytes;
@@ -321,8 +328,8 @@ __global__ __launch_bounds__(512) void prefill_kernel(
         constexpr int off = (32 * kh + 16 * cc) * kRowBytes;
 #pragma unroll
         for (int db = 0; db < 4; ++db) {
-          vr[cc][db][0] = lds_read_tr<off>(va0[db]);
-          vr[cc][db][1] = lds_read_tr<off>(va1[db]);
+          vr[cc][db][0] = lds_read_tr<off + kImm>(va0[db]);
+          vr[cc][db][1] = lds_read_tr<off + kImm>(va1[db]);
         }
       });
       if (kh == 0) {
@@ -435,10 +442,34 @@ __global__ __launch_bounds__(512) void prefill_kernel(
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   for (int kt = kt_begin; kt < min(plain_begin, kt_stop); ++kt) masked_step(kt, std::false_type{});
-  for (int kt = plain_begin; kt < plain_end; ++kt) {
-    advance(kt);
-    compute(kt * kPage, buf, std::false_type{}, std::false_type{});
-    finish(kt);
+  {
+    // the plain loop runs tile pairs on buffers (0, 1), so that every LDS buffer address
+    // is an immediate; a first tile on buffer 1 and a last one on buffer 0 run alone
+    int kt = plain_begin;
+    if (kt < plain_end && buf == 1) {
+      advance(kt);
+      compute(kt * kPage, buf, std::false_type{}, std::false_type{});
+      finish(kt);
+      ++kt;
+    }
+    for (; kt + 1 < plain_end; kt += 2) {
+      if (kt + 1 < kt_end) issue_tile(kt + 1, std::integral_constant<int, 1>{});
+      compute(kt * kPage, std::integral_constant<int, 0>{}, std::false_type{}, std::false_type{});
+      if (fp8 && kt + 1 < kt_end) store_staged(std::integral_constant<int, 1>{});
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+      if (kt + 2 < kt_end) issue_tile(kt + 2, std::integral_constant<int, 0>{});
+      compute((kt + 1) * kPage, std::integral_constant<int, 1>{}, std::false_type{}, std::false_type{});
+      if (fp8 && kt + 2 < kt_end) store_staged(std::integral_constant<int, 0>{});
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+    }
+    if (kt < plain_end) {
+      advance(kt);
+      compute(kt * kPage, buf, std::false_type{}, std::false_type{});
+      finish(kt);
+      ++kt;
+    }
   }
   for (int kt = plain_end; kt < kt_stop; ++kt) masked_step(kt, std::false_type{});
   if (tail_tile) masked_step(kt_end - 1, std::true_type{});
