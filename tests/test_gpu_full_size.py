@@ -9,6 +9,9 @@ read (copied back per sequence), so every sampled output is checked at full cont
   batch-1 decode 1 token at p = 100,000 (bf16): the row
   batched decode 32 sequences, 8K..128K keys (fp8): every row
   1M verify      8 tokens on 1,048,576 cached (fp8): every row
+  long prefill at the TP8 head share (6 query heads, 1 KV head), bf16 and fp8 caches:
+                 7 tokens per sequence, two of them straddling a 256-row tile boundary
+                 (row 8192 of 12,288 = token 1365, head 2)
 Both layer kinds run each workload."""
 
 import numpy as np
@@ -28,8 +31,8 @@ def _lib(gpu_lib):
     yield
 
 
-def _check(cfg, kind, mode, rows_of_seq, kv_dtype=None):
-    call = synth.make_config(cfg, kind, cache_device="cuda", kv_dtype=kv_dtype)
+def _check(cfg, kind, mode, rows_of_seq, kv_dtype=None, heads=None):
+    call = synth.make_config(cfg, kind, cache_device="cuda", kv_dtype=kv_dtype, heads=heads)
     say(f"case full-size config{cfg} kind={kind} mode={mode}: {call.num_seqs} seqs, "
         f"{call.num_tokens} tokens, {call.k_cache.shape[0]} pages, {call.kv_dtype}")
     s = Staged(call)
@@ -78,3 +81,10 @@ def test_batched_fp8_decode_full_size(kind):
 @pytest.mark.parametrize("kind", ["swa", "full"])
 def test_1m_verify_full_size(kind):
     _check(4, kind, "decode", lambda b, n: list(range(n)))
+
+
+@pytest.mark.parametrize("kind", ["swa", "full"])
+@pytest.mark.parametrize("kv_dtype", ["bf16", "fp8"])
+def test_long_prefill_tp8_head_share_sampled_rows(kind, kv_dtype):
+    _check(1, kind, "prefill", lambda b, n: [0, 63, 1364, 1365, 1366, 2000 + b, n - 1],
+           kv_dtype=kv_dtype, heads=(6, 1))

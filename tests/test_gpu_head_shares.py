@@ -39,6 +39,25 @@ def test_prefill_at_head_share(heads, kind, kv_dtype):
     assert_close_to_oracle(bits16(d["out"]), ref, kv_dtype, f"prefill {heads} {kind} {kv_dtype}")
 
 
+# Many (sequence, KV head) pairs of short ragged sequences over several row tiles, as in
+# a batched full-layer prefill: 200 new tokens x 6 heads = 1,200 rows = 5 row tiles for
+# each of 64 pairs (320 workgroups, more than one round on 256 CUs); shorter sequences end
+# inside their first or a middle tile.
+MANY_PAIR_CASES = [((48, 8), [200, 150, 200, 37, 200, 180, 1, 200], [900, 150, 1300, 500, 200, 2000, 64, 777]),
+               ((6, 1), [200] * 60 + [171, 1, 200, 90], [200 + 13 * i for i in range(64)])]
+
+
+@pytest.mark.parametrize("case", MANY_PAIR_CASES, ids=["hq48-hkv8-8seq", "hq6-hkv1-64seq"])
+@pytest.mark.parametrize("kv_dtype", ["bf16", "fp8"])
+def test_prefill_many_pairs(case, kv_dtype):
+    heads, q_lens, kv_lens = case
+    say(f"case prefill many pairs heads={heads} seqs={len(q_lens)} dtype={kv_dtype}")
+    call = synth.make_call(q_lens, kv_lens, "full", kv_dtype, [63, heads[0], len(q_lens)], heads=heads)
+    ref = O.layer_call(call.oracle_inputs())["y"]
+    d = run_layer(call, "prefill")
+    assert_close_to_oracle(bits16(d["out"]), ref, kv_dtype, f"prefill many pairs {heads} {kv_dtype}")
+
+
 @pytest.mark.parametrize("heads", HEADS, ids=[f"hq{a}-hkv{b}" for a, b in HEADS])
 @pytest.mark.parametrize("kind", ["swa", "full"])
 @pytest.mark.parametrize("kv_dtype", ["bf16", "fp8"])
