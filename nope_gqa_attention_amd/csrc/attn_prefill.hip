@@ -14,7 +14,7 @@
 //    its tokens. Grid: (row tile, KV head, sequence), remapped so that the row tiles of
 //    one (sequence, KV head) run on one XCD and share its L2.
 //  * K/V tiles are one 64-token page of one KV head (16 KiB each), copied straight from
-//    global memory into LDS with gfx950's global_load_lds_dwordx4 (no staging registers)
+//    global memory into LDS with buffer_load_dwordx4 ... lds (no staging registers)
 //    and double-buffered: the next page is in flight while the current one is consumed.
 //    Each 256-byte row is stored with its 16-byte chunks XOR-swizzled by the row index so
 //    that the operand reads below hit distinct LDS banks. Page numbers come from the
@@ -55,11 +55,17 @@ constexpr float kRescaleSlack = 8.0f;                    // log2 headroom before
 constexpr int kNumXcds = 8;                              // MI355X: 8 XCDs x 32 CUs
 
 typedef __attribute__((address_space(3))) void lds_void_t;
-// 16-byte direct copy global -> LDS (global_load_lds_dwordx4). A plain function, so that
-// kernel templates whose copy loops depend on template parameters still instantiate in
-// the host compilation pass.
-__device__ __forceinline__ void copy16_to_lds(const void* src, lds_void_t* dst) {
-  __builtin_amdgcn_global_load_lds(src, dst, 16, 0, 0);
+// 16-byte direct copy global -> LDS (buffer_load_dwordx4 ... lds) through a buffer
+// resource over one page tile: the base sits in scalar registers and each lane adds a
+// 32-bit offset, so the tile loop does no 64-bit per-lane address arithmetic. Plain
+// functions, so that kernel templates whose copy loops depend on template parameters
+// still instantiate in the host compilation pass.
+constexpr int kRawBufferWord3 = 0x00020000;          // raw buffer, 32-bit data format (CDNA)
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const char* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(base), 0, bytes, kRawBufferWord3);
+}
+__device__ __forceinline__ void copy16_to_lds(__amdgpu_buffer_rsrc_t r, uint32_t off, lds_void_t* dst) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, dst, 16, off, 0, 0, 0);
 }
 
 // Chunk slot of 16-byte chunk c (0..15) of row r in a swizzled tile: c XOR f(r mod 16),
@@ -136,7 +142,7 @@ __global__ __launch_bounds__(512) void prefill_kernel(
   const int g = (work / gridDim.x) % gridDim.y;
   const int b = work / (gridDim.x * gridDim.y);
   const int tid = threadIdx.x;
-  const int wave = tid / 64;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / 64);   // uniform: kept in a scalar register
   const int lane = tid % 64;
   const int half = lane / 32;      // which 8-slice of each 16-wide k step this lane feeds
   const int lr = lane % 32;        // the row (within a 32-row block) this lane owns
@@ -224,7 +230,7 @@ __global__ __launch_bounds__(512) void prefill_kernel(
   // 16 bytes = 4 rows into one contiguous 1 KiB block: lane l lands at row 4i + l/16,
   // chunk slot l%16, so it fetches that row's chunk (l%16) ^ swz_key(row).
   constexpr int kRowsCopied = kPage / kWaves;
-  int cp_off[kRowsCopied / 4];
+  uint32_t cp_off[kRowsCopied / 4];
 #pragma unroll
   for (int i = 0; i < kRowsCopied / 4; ++i) {
     const int row = kRowsCopied * wave + 4 * i + lane / 16;
@@ -253,11 +259,12 @@ __global__ __launch_bounds__(512) void prefill_kernel(
     const char* kb = static_cast<const char*>(C.k) + base;
     const char* vb = static_cast<const char*>(C.v) + base;
     if constexpr (!fp8) {
+      const __amdgpu_buffer_rsrc_t rk = tile_rsrc(kb, kTileBytes), rv = tile_rsrc(vb, kTileBytes);
 #pragma unroll
       for (int i = 0; i < kRowsCopied / 4; ++i) {
         const int dst = BUF * 2 * kTileBytes + (kRowsCopied * wave + 4 * i) * kRowBytes;
-        copy16_to_lds(kb + cp_off[i], (lds_void_t*)(lds + dst));
-        copy16_to_lds(vb + cp_off[i], (lds_void_t*)(lds + dst + kTileBytes));
+        copy16_to_lds(rk, cp_off[i], (lds_void_t*)(lds + dst));
+        copy16_to_lds(rv, cp_off[i], (lds_void_t*)(lds + dst + kTileBytes));
       }
     } else {
       // thread tid loads 16 codes (bytes 16 * (tid % 8) ..) of fp8 rows tid / 8 (+ the
