@@ -323,10 +323,8 @@ __global__ __launch_bounds__(512) void prefill_kernel(
       f32x16_t sc;
 #pragma unroll
       for (int e = 0; e < 16; ++e) sc[e] = 0.f;
-      __builtin_amdgcn_s_setprio(1);
 #pragma unroll
       for (int i = 0; i < 8; ++i) sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[i], qop[i], sc, 0, 0, 0);
-      __builtin_amdgcn_s_setprio(0);
       // V^T operands of this half (transposing reads, inline assembly: the tile has landed,
       // and the compiler would otherwise also wait for the next tile's copy in flight)
       u32x2_t vr[2][4][2];
@@ -384,7 +382,6 @@ __global__ __launch_bounds__(512) void prefill_kernel(
       lds_wait_all(vr);
       __builtin_amdgcn_sched_barrier(0);
       // ---- O^T += V^T P^T over the 32 keys of this half (2 MFMA k-steps of 16)
-      __builtin_amdgcn_s_setprio(1);
 #pragma unroll
       for (int cc = 0; cc < 2; ++cc)
 #pragma unroll
@@ -404,7 +401,6 @@ __global__ __launch_bounds__(512) void prefill_kernel(
           acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, uv), pop[cc],
                                                            acc[db], 0, 0, 0);
         }
-      __builtin_amdgcn_s_setprio(0);
     });
   };
 
