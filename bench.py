@@ -253,61 +253,108 @@ def timed_steps(parts, steps, warmup):
     return total, per
 
 
-def cpu_baseline(calls_host, budget_rows):
-    """Time the fp64 oracle on the host on a bounded sample of the prefill workload:
-    the last `budget_rows` new tokens of sequence 0 of each layer kind (kvwrite of the
-    sequence's new tokens, attention over its full visible context, gate)."""
-    import numpy as np
-
-    import oracle.beam_oracle as O
-
-    total_t, total_rows = 0.0, 0
-    for kind, inp, rows in calls_host:
-        t0 = time.perf_counter()
-        O.layer_call(inp, rows=rows)
-        total_t += time.perf_counter() - t0
-        total_rows += len(rows)
-    threads = None
+def oracle_threads():
+    """Threads the oracle's BLAS pool uses (the rest of the oracle is single-threaded numpy)."""
     try:
         from threadpoolctl import threadpool_info
-        threads = max((p.get("num_threads") or 0) for p in threadpool_info()) or None
+        return max((p.get("num_threads") or 0) for p in threadpool_info()) or os.cpu_count()
     except Exception:
-        pass
-    return total_rows, total_t, threads or os.cpu_count()
+        return os.cpu_count()
 
 
-def seq0_host_inputs(call, rows_wanted):
-    """Oracle inputs for sequence 0 of a staged call only: its pages copied to the host
-    and renumbered, so the oracle reads exactly what the GPU read."""
+def host_inputs(call, seqs, kv_head=None):
+    """Oracle inputs for sequences `seqs` of a staged call (possibly with multi-GiB caches
+    on the device): only the pages their block tables name are copied to the host and
+    renumbered densely, so the oracle reads exactly the bytes the GPU read. With kv_head
+    set, only that KV head's cache and its query heads, gate columns and gate biases are
+    kept (an exact 1/Hkv share of the attention work: heads are independent)."""
     import numpy as np
     import torch
 
-    bt = call.block_table[0]
-    pages = np.unique(bt)
-    remap = {int(p): i for i, p in enumerate(pages)}
-    idx = torch.from_numpy(pages.astype(np.int64))
-    kc = call.k_cache[idx.to(call.k_cache.device)].cpu()
-    vc = call.v_cache[idx.to(call.v_cache.device)].cpu()
-    n0 = int(call.q_start[1] - call.q_start[0])
+    seqs = list(seqs)
+    bt = np.asarray(call.block_table)[seqs]
+    pages, inv = np.unique(bt, return_inverse=True)
+    idx = torch.from_numpy(pages.astype(np.int64)).to(call.k_cache.device)
+    hkv, hq = call.num_kv_heads, call.num_q_heads
+    G = hq // hkv
+    hs = slice(0, hkv) if kv_head is None else slice(kv_head, kv_head + 1)
+    qh = slice(0, hq) if kv_head is None else slice(kv_head * G, (kv_head + 1) * G)
+    kc = call.k_cache[idx][:, hs].contiguous().cpu()
+    vc = call.v_cache[idx][:, hs].contiguous().cpu()
+    qs = np.asarray(call.q_start)
+    tok = np.concatenate([np.arange(qs[b], qs[b + 1]) for b in seqs]).astype(np.int64)
+    n = [int(qs[b + 1] - qs[b]) for b in seqs]
+    q_start = np.zeros(len(seqs) + 1, dtype=np.int32)
+    q_start[1:] = np.cumsum(n)
+    t = torch.from_numpy(tok)
 
-    def bits(t):
-        return t.view(torch.int16).numpy().view(np.uint16) if t.dtype == torch.bfloat16 else t.numpy()
+    def bits(x):
+        x = x.contiguous().cpu()
+        return x.view(torch.int16).numpy().view(np.uint16) if x.dtype == torch.bfloat16 else x.numpy()
 
-    inp = {
-        "kind": call.kind, "kv_dtype": call.kv_dtype,
-        "q_start": np.array([0, n0], dtype=np.int32), "kv_len": call.kv_len[:1],
-        "block_table": np.array([[remap[int(p)] for p in bt]], dtype=np.int32),
-        "q": bits(call.q[:n0]), "k": bits(call.k[:n0]), "v": bits(call.v[:n0]),
-        "gate": bits(call.gate[:n0]), "q_norm_w": bits(call.q_norm_w),
-        "k_norm_w": bits(call.k_norm_w), "gate_bias": bits(call.gate_bias),
-        "k_cache": bits(kc), "v_cache": bits(vc),
+    gate = call.gate[t].view(len(tok), hq, D)[:, qh].reshape(len(tok), -1)
+    return {
+        "kind": call.kind, "kv_dtype": call.kv_dtype, "q_start": q_start,
+        "kv_len": np.asarray(call.kv_len)[seqs], "block_table": inv.astype(np.int32).reshape(bt.shape),
+        "q": bits(call.q[t][:, qh]), "k": bits(call.k[t][:, hs]), "v": bits(call.v[t][:, hs]),
+        "gate": bits(gate), "q_norm_w": bits(call.q_norm_w), "k_norm_w": bits(call.k_norm_w),
+        "gate_bias": bits(call.gate_bias[qh]), "k_cache": bits(kc), "v_cache": bits(vc),
         "k_scale": call.k_scale, "v_scale": call.v_scale,
     }
-    rows = np.arange(n0 - rows_wanted, n0)
-    return inp, rows
 
 
-def run_decode(args, result):
+def time_oracle(inp, rows=None):
+    """Seconds the fp64 oracle takes for one layer call (fused prepare + K/V store of every
+    new token of `inp`, attention and gate for `rows`, all rows if None)."""
+    import oracle.beam_oracle as O
+
+    t0 = time.perf_counter()
+    O.layer_call(inp, rows=rows)
+    return time.perf_counter() - t0
+
+
+def sample_rows(q_len, kv_len, count, seed):
+    """Rows of one sequence's new tokens for a bounded oracle sample: the first and last
+    token, the tokens that open a page, then seeded random ones, `count` in all."""
+    import numpy as np
+
+    first = kv_len - q_len
+    rows = {0, q_len - 1} | {i for i in range(q_len) if (first + i) % 64 == 0}
+    rest = [i for i in range(q_len) if i not in rows]
+    rng = np.random.default_rng(seed)
+    need = max(0, count - len(rows))
+    rows |= set(int(x) for x in rng.choice(rest, size=min(need, len(rest)), replace=False))
+    return np.array(sorted(rows)[:max(count, 2)], dtype=np.int64)
+
+
+def oracle_long_prefill(staged, rows_per_seq):
+    """The oracle on the long-prefill workload, per layer kind: every sequence, KV head 0
+    and its 6 query heads, `rows_per_seq` sampled rows per sequence (all of its new tokens
+    are still normed and stored). Extrapolated to all rows and heads by the visible
+    (row, head, key) triples the sample covered, and labelled as extrapolated."""
+    out = {}
+    for kind, s in staged.items():
+        call = s.call
+        ql = [int(x) for x in call.q_lens]
+        kl = [int(x) for x in call.kv_len]
+        secs, pairs = 0.0, 0
+        for b in range(call.num_seqs):
+            inp = host_inputs(call, [b], kv_head=0)
+            rows = sample_rows(ql[b], kl[b], rows_per_seq, 1000 + b)
+            secs += time_oracle(inp, rows)
+            pairs += sum(min(kl[b] - ql[b] + int(i) + 1, 512) if kind == "swa" else kl[b] - ql[b] + int(i) + 1
+                         for i in rows)
+        frac_heads = 1.0 / call.num_kv_heads
+        total_pairs = visible_pairs(ql, kl, kind)
+        scale = (total_pairs / pairs) / frac_heads
+        out[kind] = {"sample_rows": rows_per_seq * call.num_seqs, "kv_heads_sampled": 1,
+                     "sample_s": round(secs, 2), "extrapolated_full_s": round(secs * scale, 1),
+                     "extrapolated_tokens_per_s": round(sum(ql) / (secs * scale), 3)}
+        log(f"  oracle long prefill {kind}: {out[kind]}")
+    return out
+
+
+def run_decode(args, result, oracle_out=None):
     """The decode / verify workloads: batch-1 decode at p = 100,000 (bf16), 32 sequences
     of 8K..128K keys (fp8), and an 8-token verify block on 1,048,576 keys (fp8); each as
     a full NoPE layer and an SWA-512 layer (fused norm + KV store, then split-K decode
@@ -383,10 +430,67 @@ def run_decode(args, result):
                 "hbm_frac_graph": round(nbytes / (dev_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
             }
             log(f"  decode config{cfg}-{kind}: {dec[f'config{cfg}-{kind}']}")
+            if oracle_out is not None:
+                # the oracle on the same bytes: in full, except the full layer of the two
+                # fp8 workloads, which runs on KV head 0 (an exact eighth of the work,
+                # heads being independent) and is scaled by 8
+                sample_head = 0 if (cfg in (3, 4) and kind == "full") else None
+                inp = host_inputs(call, range(call.num_seqs), kv_head=sample_head)
+                secs = time_oracle(inp)
+                full_s = secs * (call.num_kv_heads if sample_head is not None else 1)
+                oracle_out[f"config{cfg}-{kind}"] = {
+                    "s": round(full_s, 3), "tokens_per_s": round(sum(ql) / full_s, 3),
+                    "sample": ("KV head 0 of 8 (all rows, all keys), time x 8"
+                               if sample_head is not None else "in full"),
+                    "gpu_speedup": round(full_s / ((per_d["decode"] + per_d["kvwrite"]) * 1e-3), 1)}
+                log(f"  oracle config{cfg}-{kind}: {oracle_out[f'config{cfg}-{kind}']}")
+                del inp
             del s, copies, call
             torch.cuda.empty_cache()
     result["decode"] = dec
 
+
+
+def run_tiny_prefill(args, result, oracle_out=None):
+    """The tiny prefill workload (1 sequence, 1,024 new tokens, no cache) through both
+    layer kinds: launch-bound at this size, reported beside the long prefill. Timed eagerly
+    and as 20 back-to-back calls in one HIP graph (device time per call)."""
+    import torch
+
+    import synth
+
+    res = {}
+    for kind in ("full", "swa"):
+        call = synth.make_config(0, kind)
+        s = Staged(call)
+        ql = [int(x) for x in call.q_lens]
+        kl = [int(x) for x in call.kv_len]
+        _, per = timed_steps([("kvwrite", s.kvwrite), ("attn", lambda s=s: s.attend("prefill"))],
+                             max(args.steps, 10), args.warmup)
+        n_rep = 20
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for _ in range(n_rep):
+                s.attend("prefill")
+        _, pg = timed_steps([("rep", g.replay)], max(args.steps, 5), args.warmup)
+        del g
+        dev_ms = pg["rep"] / n_rep
+        fl = 4 * D * HQ * visible_pairs(ql, kl, kind)
+        res[kind] = {"prefill_us": round(per["attn"] * 1e3, 2), "kvwrite_us": round(per["kvwrite"] * 1e3, 2),
+                     "prefill_graph_us": round(dev_ms * 1e3, 2), "algorithmic_gflop": round(fl / 1e9, 3),
+                     "prefill_tflops_graph": round(fl / (dev_ms * 1e-3) / 1e12, 1),
+                     "prefill_mfma_frac_graph": round(fl / (dev_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                     "tokens_per_s": round(sum(ql) / ((per["attn"] + per["kvwrite"]) * 1e-3), 1)}
+        log(f"  tiny prefill {kind}: {res[kind]}")
+        if oracle_out is not None:
+            secs = time_oracle(host_inputs(call, [0]))
+            oracle_out[f"config0-{kind}"] = {
+                "s": round(secs, 3), "tokens_per_s": round(sum(ql) / secs, 3), "sample": "in full",
+                "gpu_speedup": round(secs / ((per["attn"] + per["kvwrite"]) * 1e-3), 1)}
+            log(f"  oracle config0-{kind}: {oracle_out[f'config0-{kind}']}")
+        del s, call
+        torch.cuda.empty_cache()
+    result["tiny_prefill"] = res
 
 
 def run_prefill_fp8(args, result):
@@ -478,7 +582,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-rows", type=int, default=200, help="oracle rows per layer kind")
+    ap.add_argument("--cpu-rows", type=int, default=64,
+                    help="oracle rows sampled per sequence of the long prefill")
     ap.add_argument("--only", choices=("all", "prefill", "decode"), default="all",
                     help="restrict the run (for counter collection); the JSON line needs 'all'")
     ap.add_argument("--summarize-counters", nargs="+", metavar="CSV",
@@ -586,32 +691,39 @@ def main():
         "layers": layers,
     }
     log(json.dumps(layers))
-    # free the prefill workload before the decode ones
-    cpu_inputs = []
-    if not args.no_cpu_baseline:
-        for kind in ("full", "swa"):
-            inp, rows = seq0_host_inputs(staged[kind].call, args.cpu_rows)
-            cpu_inputs.append((kind, inp, rows))
+    oracle_times = None if args.no_cpu_baseline else {}
+    if oracle_times is not None:
+        # the oracle on the same bytes, per layer kind, on a bounded sample
+        log("timing the fp64 oracle on the host (long prefill, sampled) ...")
+        olp = oracle_long_prefill(staged, args.cpu_rows)
+        total_s = sum(v["extrapolated_full_s"] for v in olp.values())
+        step_s = {k: (layers[k]["ms"]) * 1e-3 for k in layers}
+        for k in olp:
+            olp[k]["gpu_speedup"] = round(olp[k]["extrapolated_full_s"] / step_s[k], 1)
+        result["cpu_baseline"] = {
+            "value": round(new_tokens / total_s, 3), "unit": "tokens/s", "cores": oracle_threads(),
+            "kind": "oracle",
+            "sample": (f"{args.cpu_rows} sampled new tokens per sequence (first, last, page starts, "
+                       f"seeded random) of all 8 sequences, on KV head 0 and its 6 query heads, per "
+                       f"layer kind (prepare + K/V store of every new token of the sequence, "
+                       f"attention over the full visible context, gate); times scaled to all "
+                       f"16,384 tokens and 48 heads by visible (row, head, key) triples: "
+                       f"extrapolated, measured sample "
+                       f"{sum(v['sample_s'] for v in olp.values()):.1f} s"),
+            "per_layer": olp,
+        }
     del staged, parts
     torch.cuda.empty_cache()
 
     if not args.no_decode and args.only == "all":  # "--only prefill" skips the decode workloads
-        run_decode(args, result)
+        run_tiny_prefill(args, result, oracle_times)
+        run_decode(args, result, oracle_times)
         run_prefill_fp8(args, result)
         run_head_share(args, result)
     if args.only in ("all", "prefill"):
         run_projections(args, result, new_tokens)
-
-    # ---------------------------------------------------------------- oracle on the host
-    if not args.no_cpu_baseline:
-        log("timing the fp64 oracle on the host ...")
-        rows, secs, cores = cpu_baseline(cpu_inputs, args.cpu_rows)
-        result["cpu_baseline"] = {
-            "value": round(rows / secs, 3), "unit": "tokens/s", "cores": cores, "kind": "oracle",
-            "sample": f"last {args.cpu_rows} new tokens of sequence 0 in each layer kind "
-                      f"(full over 100,352 keys, SWA over 512), incl. that sequence's "
-                      f"kvwrite of 2048 tokens; {secs:.1f} s total",
-        }
+    if oracle_times is not None:
+        result["oracle_timings"] = {"cores": oracle_threads(), "configs": oracle_times}
     print(json.dumps(result), flush=True)
 
 

@@ -150,9 +150,10 @@ beam_status beam_qknorm_rope_ssmax_kvwrite(const beam_layer_desc* layer, const b
                                            int64_t norm_w_head_stride,
                                            void* q_out, int64_t q_out_stride, void* stream);
 
-/* Causal prefill attention over the paged cache (bf16 cache only), MFMA bf16 with fp32
- * softmax, GQA (query head h reads KV head h / (num_q_heads/num_kv_heads)), optional
- * fused output gate.
+/* Causal prefill attention over the paged cache ("Reflection Beam 1.0 on vLLM", section
+ * "Attention: sliding-window layers plus NoPE full-attention layers"), bf16 or fp8-e4m3
+ * cache, MFMA bf16 with fp32 softmax, GQA (query head h reads KV head
+ * h / (num_q_heads/num_kv_heads)), optional fused output gate.
  *  q     device bf16 q' from beam_qknorm_rope_ssmax_kvwrite, [num_tokens][Hq][D], stride q_stride
  *  gate  device bf16 [num_tokens][Hq*D], token stride gate_stride, or NULL for no gate
  *  gate_bias device bf16 [Hq] (ignored when gate is NULL)
@@ -173,6 +174,12 @@ beam_status beam_attn_prefill(const beam_layer_desc* layer, const beam_batch* ba
 
 /* Decode / speculative-verify attention: the same result as beam_attn_prefill for
  * 1..16 new tokens per sequence (causal within the block), over a bf16 or fp8 cache.
+ * Defined by "Reflection Beam 1.0 on vLLM", section "Attention: sliding-window layers
+ * plus NoPE full-attention layers" (what each layer kind attends to), and by "SGLang
+ * natively supports Reflection's Beam", DFlash2 section (a drafted block of tokens is
+ * checked by one forward of the target model, so its tokens attend causally among
+ * themselves on top of the cached prefix). An empty batch (num_seqs == 0) launches
+ * nothing and returns BEAM_OK.
  * The keys are split into chunks processed in parallel; partial (max, sum, output)
  * triples go to `workspace` (device, at least beam_attn_decode_workspace_bytes(...)
  * bytes, 256-byte aligned; its contents need no initialisation and are scratch after
@@ -185,13 +192,15 @@ beam_status beam_attn_decode(const beam_layer_desc* layer, const beam_batch* bat
                              void* out, int64_t out_stride,
                              void* workspace, size_t workspace_bytes, void* stream);
 
-/* Workspace bytes beam_attn_decode needs for these host bounds (0 on invalid input). */
+/* Workspace bytes beam_attn_decode needs for these host bounds (0 on invalid input and
+ * for an empty batch). */
 size_t beam_attn_decode_workspace_bytes(const beam_layer_desc* layer, int32_t num_seqs,
                                         int32_t max_q_len, int64_t max_kv_len);
 
-/* Standalone output gate ("Attention: ..." of the vLLM page: each head's output is
- * multiplied by sigmoid(gate + per-head bias) before o_proj; "Fusion optimizations" of
- * the SGLang page fuse bias add, sigmoid and multiply):
+/* Standalone output gate ("Attention: sliding-window layers plus NoPE full-attention
+ * layers" of the vLLM page: a sigmoid of the gate projection plus a per-head bias scales
+ * each head's output ahead of o_proj; "Fusion optimizations" of the SGLang page: one
+ * kernel for the bias add, sigmoid and product):
  *  out[t,h,d] = bf16(attn[t,h,d] * sigmoid(gate[t,h*D+d] + gate_bias[h])), fp32 math.
  *  attn, out device bf16 [num_tokens][Hq][D] (token strides attn_stride, out_stride; out may
  *  equal attn); gate device bf16 [num_tokens][Hq*D]; gate_bias device bf16 [Hq]. */

@@ -57,6 +57,14 @@ beam::DecodeSplit choose_decode_split(int32_t G, int32_t kind, int32_t window, i
                                       int32_t max_q_len, int64_t max_kv_len, int32_t Hkv,
                                       int32_t kv_dtype) {
   beam::DecodeSplit s{};
+  s.num_splits = 1;
+  s.row_chunks = 1;
+  s.rows_per_chunk = 16;
+  s.keys_per_split = beam::kDecodeKeysPerBlockStep;
+  s.waves = beam::kDecodeWaves;
+  // an empty batch launches nothing: any geometry will do, and the one above needs no
+  // workspace (the sizing below would otherwise divide by zero workgroups per split)
+  if (num_seqs <= 0 || max_q_len <= 0) return s;
   const int64_t rows = (int64_t)G * max_q_len;
   s.row_chunks = (int32_t)((rows + beam::kDecodeMaxRowsPerChunk - 1) / beam::kDecodeMaxRowsPerChunk);
   if (s.row_chunks < 1) s.row_chunks = 1;
@@ -339,6 +347,7 @@ size_t beam_attn_decode_workspace_bytes(const beam_layer_desc* layer, int32_t nu
   beam::LayerParams L;
   if (check_layer(layer, &L) != BEAM_OK) return 0;
   if (num_seqs < 0 || max_q_len < 1 || max_q_len > 16 || max_kv_len < max_q_len) return 0;
+  if (num_seqs == 0) return 0;   // an empty batch launches nothing
   // the split depends on the cache dtype (resident workgroups per CU): size for either
   size_t need = 0;
   for (int32_t dt : {(int32_t)BEAM_KV_BF16, (int32_t)BEAM_KV_FP8_E4M3}) {
@@ -364,6 +373,7 @@ beam_status beam_attn_decode(const beam_layer_desc* layer, const beam_batch* bat
   if ((s = check_cache(cache, &C)) != BEAM_OK) return s;
   if (B.max_q_len < 1 || B.max_q_len > 16)
     return fail(BEAM_ERR_INVALID_ARG, "decode needs max_q_len in 1..16 (got %d)", B.max_q_len);
+  if (B.num_seqs == 0) return ok();   // an empty batch (e.g. every sequence finished)
   const int64_t N = B.num_tokens;
   const int64_t row = (int64_t)L.Hq * beam::kHeadDim;
   if ((s = check_tensor("q", q, q_stride, row, N)) != BEAM_OK) return s;

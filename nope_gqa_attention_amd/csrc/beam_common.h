@@ -132,9 +132,12 @@ __device__ __forceinline__ uint32_t bf16_bits_rne(float f) {
 }
 
 // OCP E4M3FN encode with saturation: |x| >= 448 -> +-448, NaN -> 0x7F, otherwise the
-// nearest representable value with ties to even mantissa. Written from the format: 4
-// exponent bits with bias 7 (normals 2^-6 .. 2^8), 3 mantissa bits, subnormals M * 2^-9.
-__device__ __forceinline__ uint32_t f32_to_e4m3_sat(float x) {
+// nearest representable value. Written from the format: 4 exponent bits with bias 7
+// (normals 2^-6 .. 2^8), 3 mantissa bits, subnormals M * 2^-9. x is a rounded stand-in
+// for an exact value; `dir` says where that exact value lies when x sits exactly on a
+// midpoint between two codes: > 0 beyond |x| (round the magnitude up), < 0 short of it
+// (round down), 0 on it (ties to the even mantissa).
+__device__ __forceinline__ uint32_t f32_to_e4m3_sat(float x, int dir = 0) {
   const uint32_t u = __float_as_uint(x);
   const uint32_t sign = (u >> 24) & 0x80u;
   const uint32_t a = u & 0x7FFFFFFFu;
@@ -144,14 +147,31 @@ __device__ __forceinline__ uint32_t f32_to_e4m3_sat(float x) {
   if (e >= -6) {                                       // normal range of e4m3
     uint32_t q = (a >> 20) & 7u;                       // top 3 mantissa bits
     const uint32_t rem = a & 0xFFFFFu;
-    const uint32_t up = (rem > 0x80000u) || (rem == 0x80000u && (q & 1u));
+    const uint32_t up = (rem > 0x80000u) ||
+                        (rem == 0x80000u && (dir > 0 || (dir == 0 && (q & 1u))));
     uint32_t code = ((uint32_t)(e + 7) << 3) + q + up;   // carry into exponent is exact
     return sign | code;
   }
-  // subnormal: value / 2^-9 rounded to an integer (ties to even); 8 becomes 2^-6 (0x08)
+  // subnormal: value / 2^-9 rounded to an integer; 8 becomes 2^-6 (0x08)
   const float t = __uint_as_float(a) * 512.0f;         // exact power-of-two scaling
-  const uint32_t m = (uint32_t)__builtin_rintf(t);
+  const float fl = __builtin_floorf(t);
+  uint32_t m;
+  if (t - fl == 0.5f && dir != 0) m = (uint32_t)fl + (dir > 0 ? 1u : 0u);
+  else m = (uint32_t)__builtin_rintf(t);                // ties to even
   return sign | m;
+}
+
+// e4m3 code of the exact quotient x / scale (scale finite and > 0), i.e. the nearest
+// code to the real number x / scale, not to its binary32 rounding. The binary32
+// quotient q keeps the exact quotient's side of every e4m3 midpoint (midpoints are
+// binary32 numbers, and rounding is monotone), but it can land on one. The remainder
+// x - q * scale is exact in binary32 (one fma, q correctly rounded) and its sign says
+// on which side of q the exact quotient lies, which settles such a landing.
+__device__ __forceinline__ uint32_t e4m3_of_quotient(float x, float scale) {
+  const float q = x / scale;                 // correctly rounded (IEEE division)
+  const float r = __builtin_fmaf(-q, scale, x);
+  const int dir = (r == 0.0f || q == 0.0f) ? 0 : (((r > 0.0f) == (q > 0.0f)) ? 1 : -1);
+  return f32_to_e4m3_sat(q, dir);
 }
 
 // Wave-wide helpers (wave64).

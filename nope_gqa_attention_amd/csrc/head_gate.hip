@@ -1,10 +1,10 @@
 // Standalone sigmoid output gate: out[t,h,d] = attn[t,h,d] * sigmoid(gate[t,h*D+d] + bias[h]).
 //
 // What it computes: "Reflection Beam 1.0 on vLLM", section "Attention: sliding-window
-// layers plus NoPE full-attention layers" (each head's output is multiplied by
-// sigma(gate + per-head bias), the gate coming from its own full-width projection, so a
-// head can be switched off token by token), and "SGLang natively supports Reflection's
-// Beam", section "Fusion optimizations" (bias add, sigmoid and multiply in one kernel).
+// layers plus NoPE full-attention layers" (a per-element sigmoid gate with a bias per
+// head, fed by a projection of its own, scales every head's output, which lets a token
+// silence a head), and "SGLang natively supports Reflection's Beam", section "Fusion
+// optimizations" (the three elementwise steps in one kernel).
 // The attention kernels apply the same gate in their epilogues; this entry point serves
 // callers that keep attention and gate apart.
 //

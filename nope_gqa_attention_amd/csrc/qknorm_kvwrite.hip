@@ -138,13 +138,14 @@ __global__ __launch_bounds__(kThreads) void qknorm_kvwrite_kernel(
         u32x4_t o = {out_bits[0], out_bits[1], out_bits[2], out_bits[3]};
         *reinterpret_cast<u32x4_t*>(dst + off) = o;
       } else {
-        // the stored value is the bf16-rounded one, divided by the tensor scale
+        // the stored value is the bf16-rounded one over the tensor scale: the code of the
+        // exact quotient
         const float scale = is_k ? C.k_scale : C.v_scale;
         uint32_t codes[2] = {0u, 0u};
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
           const uint32_t h16 = (out_bits[j / 2] >> (16 * (j % 2))) & 0xFFFFu;
-          const uint32_t c = f32_to_e4m3_sat(bf16_to_f32(h16) / scale);
+          const uint32_t c = e4m3_of_quotient(bf16_to_f32(h16), scale);
           codes[j / 4] |= c << (8 * (j % 4));
         }
         uint8_t* dst = static_cast<uint8_t*>(is_k ? C.k : C.v);

@@ -33,7 +33,9 @@ Readings taken where the pages are silent (each is listed in the design notes):
   * gate column h*128 + d; per-head bias broadcast over d; V is not normalised.
   * New tokens in one call see earlier new tokens and themselves (causal block).
   * fp8 is OCP E4M3FN with saturating round-to-nearest-even; stored = e4m3(k'/scale),
-    the quotient formed as one binary32 division (the precision that decides the code).
+    the quotient value/scale formed in fp64. A bf16 value over an fp32 scale is never
+    within 2^-53 (relative) of an e4m3 rounding midpoint without lying on it, so this
+    code is the nearest e4m3 value to the exact quotient.
 
 Parity status: every function below is pinned by the CPU test-suite against closed
 forms, library routines or invariants, except the readings above that no page fixes
@@ -108,7 +110,7 @@ def f64_to_bf16_bits(x) -> np.ndarray:
     return (r.view(np.uint32) >> np.uint32(16)).astype(np.uint16)
 
 
-def e4m3_to_f64(codes) -> np.ndarray:
+def _e4m3_formula(codes) -> np.ndarray:
     """Value of OCP FP8 E4M3FN codes: sign, 4 exponent bits (bias 7), 3 mantissa bits.
 
     Exponent field 0 holds subnormals M/8 * 2^-6; S.1111.111 is NaN; there is no inf.
@@ -120,6 +122,15 @@ def e4m3_to_f64(codes) -> np.ndarray:
     val = np.where(e == 0, m / 8.0 * 2.0 ** -6, (1.0 + m / 8.0) * np.ldexp(1.0, e - 7))
     val = s * val
     return np.where((e == 15) & ((c & 7) == 7), np.nan, val)
+
+
+# the value of every one of the 256 codes, from the formula above
+_E4M3_ALL_VALUES = _e4m3_formula(np.arange(256, dtype=np.uint8))
+
+
+def e4m3_to_f64(codes) -> np.ndarray:
+    """Value of OCP FP8 E4M3FN codes (the formula above, looked up per code)."""
+    return _E4M3_ALL_VALUES[np.asarray(codes, dtype=np.uint8)]
 
 
 _E4M3_POS_CODES = np.arange(0, 0x7F, dtype=np.uint8)          # +0 .. +448, NaN excluded
@@ -249,21 +260,17 @@ def physical_slot(block_table, b, pos, page_size: int = PAGE_SIZE):
 def store_kv(cache, block_table, seq, pos, values_bits, kv_dtype: str, scale: float = 1.0):
     """Write new K (or V) rows into a copy of `cache` at their physical slots.
     values_bits: [N, Hkv, D] bf16 bits (k' after norm/rotation, or raw v).
-    bf16 cache stores the bits unchanged; fp8 cache stores e4m3(value / scale).
-
-    The fp8 code is an integer decided by floating point: value / scale is formed as
-    one IEEE binary32 division (the kernel's precision; the pages fix none) and that
-    quotient is rounded to e4m3. Forming it in fp64 instead moves about 1% of codes by
-    one step: the scale amax/448 is itself an fp32 rounding, so quotients fall within
-    2^-24 of an e4m3 midpoint far more often than chance.
+    bf16 cache stores the bits unchanged; fp8 cache stores e4m3(value / scale), the
+    quotient of the bf16 value and the fp32 scale formed in fp64 and rounded once to
+    e4m3 (saturating, ties to even).
     """
     out = np.array(cache, copy=True)
     page, slot = physical_slot(block_table, seq, pos)
     if kv_dtype == "bf16":
         out[page, :, slot, :] = np.asarray(values_bits, dtype=np.uint16)
     elif kv_dtype == "fp8":
-        quotient = bf16_bits_to_f64(values_bits).astype(np.float32) / np.float32(scale)
-        out[page, :, slot, :] = f64_to_e4m3(quotient.astype(np.float64))
+        quotient = bf16_bits_to_f64(values_bits) / float(np.float32(scale))
+        out[page, :, slot, :] = f64_to_e4m3(quotient)
     else:
         raise ValueError(kv_dtype)
     return out

@@ -59,6 +59,31 @@ int main(void) {
   CHECK(beam_head_gate(&full, 4, NULL, 6144, NULL, 6144, NULL, NULL, 6144, NULL) ==
         BEAM_ERR_INVALID_ARG);
 
+  /* an empty batch (every sequence finished) sizes no workspace and launches nothing;
+   * the cache and tensor pointers are never dereferenced on this path */
+  CHECK(beam_attn_decode_workspace_bytes(&full, 0, 1, 100000) == 0);
+  CHECK(beam_attn_decode_workspace_bytes(&swa, 0, 16, 1048584) == 0);
+  {
+    static uint64_t fake[64]; /* 16-byte aligned host storage standing in for device buffers */
+    beam_kv_cache cache;
+    beam_batch empty;
+    memset(&cache, 0, sizeof cache);
+    memset(&empty, 0, sizeof empty);
+    cache.k = fake;
+    cache.v = fake + 32;
+    cache.num_pages = 1;
+    cache.dtype = BEAM_KV_BF16;
+    empty.num_seqs = 0;
+    empty.max_pages = 1563;
+    empty.max_q_len = 1;
+    empty.max_kv_len = 100000;
+    empty.num_tokens = 0;
+    CHECK(beam_attn_decode(&full, &empty, &cache, NULL, 6144, NULL, 6144, NULL, NULL, 6144, NULL, 0,
+                           NULL) == BEAM_OK);
+    CHECK(beam_attn_decode(&swa, &empty, &cache, NULL, 6144, NULL, 6144, NULL, NULL, 6144, NULL, 0,
+                           NULL) == BEAM_OK);
+  }
+
   if (!failures) printf("ok\n");
   return failures;
 }

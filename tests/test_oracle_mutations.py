@@ -77,7 +77,51 @@ def _bf16_truncate(x):
     return (x.view(np.uint32) & np.uint32(0xFFFF0000)).view(np.float32).astype(np.float64)
 
 
+def _store_binary32_quotient(cache, block_table, seq, pos, values_bits, kv_dtype, scale=1.0):
+    out = np.array(cache, copy=True)
+    page, slot = B.physical_slot(block_table, seq, pos)
+    if kv_dtype == "bf16":
+        out[page, :, slot, :] = np.asarray(values_bits, dtype=np.uint16)
+    else:
+        q = B.bf16_bits_to_f64(values_bits).astype(np.float32) / np.float32(scale)
+        out[page, :, slot, :] = B.f64_to_e4m3(q.astype(np.float64))
+    return out
+
+
+def _prepare(x_bits, w_bits, pos, kind, is_query, order):
+    """prepare_qk with the sliding-layer steps in a wrong order: 'rotate-first' applies
+    RoPE before the norm, 'round-between' rounds to bf16 after the norm and again after
+    the rotation."""
+    x = B.bf16_bits_to_f64(x_bits)
+    w = B.bf16_bits_to_f64(w_bits)
+    w = w[None, None, :] if w.ndim == 1 else w[None, :, :]
+    pos = np.asarray(pos, dtype=np.int64)
+    if kind != B.KIND_SWA:
+        y = B.rms_norm(x, w)
+        if is_query:
+            y = y * B.ssmax_scale(pos + 1)[:, None, None]
+        return B.f64_to_bf16_bits(y)
+    if order == "rotate-first":
+        y = B.rms_norm(B.rope(x, pos[:, None]), w)
+    else:
+        y = B.rope(B.bf16_round(B.rms_norm(x, w)), pos[:, None])
+    return B.f64_to_bf16_bits(y)
+
+
+_ORIG_BF16_ROUND = B.bf16_round
+
+
+def _bf16_round_via_binary32(x):
+    return _ORIG_BF16_ROUND(np.asarray(x, dtype=np.float64).astype(np.float32).astype(np.float64))
+
+
 MUTATIONS = [
+    ("store_kv", _store_binary32_quotient, pins.test_fp8_store_is_nearest_e4m3_of_exact_quotient),
+    ("prepare_qk", lambda *a, **k: _prepare(*a, order="rotate-first"),
+     pins.test_prepare_k_sliding_layer_is_norm_then_rotation_then_one_rounding),
+    ("prepare_qk", lambda *a, **k: _prepare(*a, order="round-between"),
+     pins.test_prepare_k_sliding_layer_is_norm_then_rotation_then_one_rounding),
+    ("bf16_round", _bf16_round_via_binary32, pins.test_bf16_round_of_f64_is_one_rounding),
     ("visible_range", _window_off_by_one, pins.test_window_equals_full_up_to_512_keys_and_differs_after),
     ("attend", _attend_wrong_group, pins.test_attention_matches_sdpa_textbook_routine),
     ("rope", _rope_wrong_sign, lambda: pins.test_rope_frequencies_and_direction(16, 0.1)),
