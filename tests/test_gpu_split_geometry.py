@@ -53,6 +53,24 @@ def _with_bounds(call, max_q_len, max_kv_len):
     return b
 
 
+def _agreement(a_bits, b_bits, what, check=True):
+    """Agreement of two bf16 outputs of the same call. Splitting changes the fp32 order of
+    the sums and the running maxima against which each softmax weight is rounded to bf16
+    for the P.V product, so two geometries differ by rounding only: at most one bf16 step
+    at the larger of the two magnitudes, or at 2^-4 where the output is smaller (sums that
+    cancel), and a mean difference far inside the oracle's mean tolerance."""
+    a, b = O.bf16_bits_to_f64(a_bits), O.bf16_bits_to_f64(b_bits)
+    steps = np.abs(ordered16(a_bits) - ordered16(b_bits))
+    mag = np.maximum(np.maximum(np.abs(a), np.abs(b)), 2.0 ** -4)
+    step = np.exp2(np.floor(np.log2(mag)) - 7)
+    d = np.abs(a - b)
+    say(f"  {what}: bit-equal {np.mean(steps == 0):.5f}, max diff in bf16 steps at max(|y|, 2^-4) "
+        f"{(d / step).max():.3f}, max-abs diff {d.max():.3e}, mean-abs {d.mean():.3e}")
+    if check:
+        assert np.all(d <= step)
+        assert d.mean() <= 1e-4
+
+
 @pytest.mark.parametrize("kv_dtype", ["bf16", "fp8"])
 @pytest.mark.parametrize("name,kind,q_lens,kv_lens,bounds", CASES, ids=[c[0] for c in CASES])
 def test_decode_agrees_across_split_geometries(name, kind, q_lens, kv_lens, bounds, kv_dtype):
@@ -75,14 +93,11 @@ def test_decode_agrees_across_split_geometries(name, kind, q_lens, kv_lens, boun
         torch.cuda.synchronize()
         assert np.array_equal(bits16(d["out"]), outs[-1]), "not reproducible under one geometry"
     for i, o in enumerate(outs[1:], 1):
-        diff = np.abs(ordered16(o) - ordered16(outs[0]))
-        say(f"  geometry {i} vs 0: max {diff.max()} bf16 steps, bit-equal {np.mean(diff == 0):.5f}")
-        assert diff.max() <= 1 and np.mean(diff == 0) >= 0.99
+        _agreement(o, outs[0], f"geometry {i} vs 0")
     # prefill over the same tokens: another kernel, the same definition
     d["batch"] = _with_bounds(call, None, None)
     run_attend(d, "prefill")
     torch.cuda.synchronize()
     pf = bits16(d["out"])
     assert_close_to_oracle(pf, ref["y"], kv_dtype, f"{name} prefill")
-    diff = np.abs(ordered16(pf) - ordered16(outs[0]))
-    say(f"  prefill vs decode: max {diff.max()} bf16 steps, bit-equal {np.mean(diff == 0):.5f}")
+    _agreement(pf, outs[0], "prefill vs decode", check=False)
