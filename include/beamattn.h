@@ -14,7 +14,8 @@
  *  - Plain C ABI. Pointers marked "device" are device memory of the current HIP device;
  *    pointers marked "host" are host memory read before the call returns. The caller
  *    owns every buffer; the library keeps no pointer after a call returns, allocates
- *    nothing, holds no mutable global state, and is safe to call from several threads.
+ *    nothing, and is safe to call from several threads. Its only mutable global state is
+ *    the per-device address of the scratch array of beam_attn_decode_noalloc.
  *  - `stream` is a hipStream_t passed as void*; NULL means the null stream. Every call
  *    only enqueues work on it and returns; nothing synchronises.
  *  - Element types: bf16 tensors are 16-bit bfloat16 values; fp8 caches hold OCP E4M3FN
@@ -196,6 +197,27 @@ beam_status beam_attn_decode(const beam_layer_desc* layer, const beam_batch* bat
  * for an empty batch). */
 size_t beam_attn_decode_workspace_bytes(const beam_layer_desc* layer, int32_t num_seqs,
                                         int32_t max_q_len, int64_t max_kv_len);
+
+/* Bytes of the device scratch array behind beam_attn_decode_noalloc (32 MiB per device). */
+#define BEAM_DECODE_NOALLOC_SCRATCH_BYTES (32u * 1024u * 1024u)
+
+/* beam_attn_decode without a workspace argument, for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc. Same arguments, checks, kernels and results as beam_attn_decode (bit for
+ * bit); the split partials go to a file-scope device array of
+ * BEAM_DECODE_NOALLOC_SCRATCH_BYTES that each device the library runs on holds until the
+ * process ends. The call allocates nothing (no hipMalloc, no allocating library call).
+ * Returns BEAM_ERR_WORKSPACE, launching nothing, when the host bounds need more scratch
+ * than that (beam_attn_decode_workspace_bytes tells the need; e.g. 32 sequences of up to
+ * 131,072 keys, or one 16-token block over 1,048,584 keys, fit). The scratch needs no
+ * initialisation. Every call on one device shares that device's scratch and leaves its
+ * partials there: calls that may overlap in time on one device (several streams, several
+ * threads) race and must be serialised by the caller. Debug builds do not run their
+ * batch-metadata check in this entry point (that check allocates). */
+beam_status beam_attn_decode_noalloc(const beam_layer_desc* layer, const beam_batch* batch,
+                                     const beam_kv_cache* cache, const void* q, int64_t q_stride,
+                                     const void* gate, int64_t gate_stride, const void* gate_bias,
+                                     void* out, int64_t out_stride, void* stream);
 
 /* Standalone output gate ("Attention: sliding-window layers plus NoPE full-attention
  * layers" of the vLLM page: a sigmoid of the gate projection plus a per-head bias scales

@@ -28,7 +28,8 @@ BEAM_KV_BF16, BEAM_KV_FP8_E4M3 = 0, 1
 
 ENTRY_POINTS = (
     "beam_qknorm_rope_ssmax_kvwrite", "beam_attn_prefill", "beam_attn_decode",
-    "beam_attn_decode_workspace_bytes", "beam_head_gate", "beam_linear_bf16",
+    "beam_attn_decode_noalloc", "beam_attn_decode_workspace_bytes", "beam_head_gate",
+    "beam_linear_bf16",
     "beam_kv_bytes_per_token",
     "beam_status_string", "beam_last_error", "beam_abi_version",
 )
@@ -99,6 +100,10 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         P(LayerDesc), P(Batch), P(KVCache), c_void_p, c_int64, c_void_p, c_int64, c_void_p,
         c_void_p, c_int64, c_void_p, c_size_t, c_void_p]
     lib.beam_attn_decode.restype = c_int32
+    lib.beam_attn_decode_noalloc.argtypes = [
+        P(LayerDesc), P(Batch), P(KVCache), c_void_p, c_int64, c_void_p, c_int64, c_void_p,
+        c_void_p, c_int64, c_void_p]
+    lib.beam_attn_decode_noalloc.restype = c_int32
     lib.beam_attn_decode_workspace_bytes.argtypes = [P(LayerDesc), c_int32, c_int32, c_int64]
     lib.beam_attn_decode_workspace_bytes.restype = c_size_t
     lib.beam_head_gate.argtypes = [
@@ -256,6 +261,24 @@ def beam_attn_decode(layer: LayerDesc, batch: DeviceBatch, cache: DeviceCache, q
     _check(lib.beam_attn_decode(
         ctypes.byref(layer), ctypes.byref(b), ctypes.byref(c), qp, qs, gp, gs,
         c_void_p(gate_bias.data_ptr() if gate_bias is not None else None), op, os_, wp, wb,
+        _stream(stream)))
+
+
+BEAM_DECODE_NOALLOC_SCRATCH_BYTES = 32 * 1024 * 1024
+
+
+def beam_attn_decode_noalloc(layer: LayerDesc, batch: DeviceBatch, cache: DeviceCache, q, gate,
+                             gate_bias, out, stream=None):
+    """beam_attn_decode with the split partials in the library's per-device scratch array
+    (no workspace argument, no allocation)."""
+    lib = load()
+    qp, qs = _tok(q, "q")
+    gp, gs = _tok(gate, "gate")
+    op, os_ = _tok(out, "out")
+    b, c = batch.struct(), cache.struct()
+    _check(lib.beam_attn_decode_noalloc(
+        ctypes.byref(layer), ctypes.byref(b), ctypes.byref(c), qp, qs, gp, gs,
+        c_void_p(gate_bias.data_ptr() if gate_bias is not None else None), op, os_,
         _stream(stream)))
 
 

@@ -1,13 +1,15 @@
 // C ABI of libbeamattn: validates every host-visible argument, then launches the HIP
 // kernels on the caller's stream. No allocation, no synchronisation, no global mutable
-// state except the thread-local last-error message (debug builds add a synchronous
-// check of the device-resident batch metadata, see debug_check_batch).
+// state except the thread-local last-error message and the per-device address table of
+// the allocation-free decode's scratch array (debug builds add a synchronous check of
+// the device-resident batch metadata, see debug_check_batch).
 #include <hip/hip_runtime.h>
 
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 
 #include "beam_common.h"
 #include "beamattn.h"
@@ -272,6 +274,38 @@ beam_status debug_check_batch(const beam::LayerParams& L, const beam::BatchParam
   } while (0)
 #endif
 
+// ---- scratch of the allocation-free decode entry point. The split partials go into this
+// file-scope device array instead of a caller workspace; every device the library runs on
+// holds its own copy for the life of the process. In host code `scratch` names only a
+// host-side stand-in symbol: its device address on the current device comes from
+// hipGetSymbolAddress, taken once per device and kept in g_scratch_addr.
+constexpr size_t kNoAllocScratchBytes = BEAM_DECODE_NOALLOC_SCRATCH_BYTES;
+__device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_addr[kMaxDevices] = {};
+
+beam_status scratch_on_current_device(void** addr) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(BEAM_ERR_HIP, "hipGetDevice failed: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(BEAM_ERR_UNSUPPORTED, "device index %d is beyond the %d this library tracks", dev,
+                kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_addr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || p == nullptr)
+      return fail(BEAM_ERR_HIP, "hipGetSymbolAddress(scratch) failed on device %d: %s", dev,
+                  hipGetErrorString(e));
+    g_scratch_addr[dev] = p;
+  }
+  *addr = g_scratch_addr[dev];
+  return BEAM_OK;
+}
+
 bool ranges_overlap(const void* a, int64_t a_bytes, const void* b, int64_t b_bytes) {
   const uintptr_t pa = reinterpret_cast<uintptr_t>(a), pb = reinterpret_cast<uintptr_t>(b);
   return pa < pb + (uintptr_t)b_bytes && pb < pa + (uintptr_t)a_bytes;
@@ -359,11 +393,18 @@ size_t beam_attn_decode_workspace_bytes(const beam_layer_desc* layer, int32_t nu
   return need;
 }
 
-beam_status beam_attn_decode(const beam_layer_desc* layer, const beam_batch* batch,
-                             const beam_kv_cache* cache, const void* q, int64_t q_stride,
-                             const void* gate, int64_t gate_stride, const void* gate_bias,
-                             void* out, int64_t out_stride, void* workspace,
-                             size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Shared body of the two decode entry points. scratch_mode: the partials go to the
+// file-scope scratch array (no caller workspace, no allocation, no batch-metadata check
+// even in debug builds, since that check allocates).
+beam_status attn_decode(const beam_layer_desc* layer, const beam_batch* batch,
+                        const beam_kv_cache* cache, const void* q, int64_t q_stride,
+                        const void* gate, int64_t gate_stride, const void* gate_bias, void* out,
+                        int64_t out_stride, void* workspace, size_t workspace_bytes,
+                        bool scratch_mode, void* stream) {
   beam::LayerParams L;
   beam::BatchParams B;
   beam::CacheParams C;
@@ -382,17 +423,48 @@ beam_status beam_attn_decode(const beam_layer_desc* layer, const beam_batch* bat
   const beam::DecodeSplit S = choose_decode_split(L.G, L.kind, L.window, B.num_seqs, B.max_q_len,
                                                   B.max_kv_len, L.Hkv, C.dtype);
   const size_t need = decode_workspace_bytes(S, B.num_seqs, B.max_q_len, L.Hq);
-  if (need > 0) {
-    if (!workspace || workspace_bytes < need)
-      return fail(BEAM_ERR_WORKSPACE, "decode workspace needs %zu bytes (got %zu%s)", need,
-                  workspace_bytes, workspace ? "" : ", NULL pointer");
-    if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
-      return fail(BEAM_ERR_INVALID_ARG, "decode workspace must be 256-byte aligned");
+  if (scratch_mode) {
+    workspace = nullptr;
+    if (need > kNoAllocScratchBytes)
+      return fail(BEAM_ERR_WORKSPACE,
+                  "allocation-free decode needs %zu bytes of scratch for these bounds; its "
+                  "scratch holds %zu (use beam_attn_decode with a workspace)",
+                  need, kNoAllocScratchBytes);
+    if (need > 0 && (s = scratch_on_current_device(&workspace)) != BEAM_OK) return s;
+  } else {
+    if (need > 0) {
+      if (!workspace || workspace_bytes < need)
+        return fail(BEAM_ERR_WORKSPACE, "decode workspace needs %zu bytes (got %zu%s)", need,
+                    workspace_bytes, workspace ? "" : ", NULL pointer");
+      if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+        return fail(BEAM_ERR_INVALID_ARG, "decode workspace must be 256-byte aligned");
+    }
+    BEAM_DEBUG_CHECK_BATCH(L, B, C, stream);
   }
-  BEAM_DEBUG_CHECK_BATCH(L, B, C, stream);
   return launched(beam::launch_attn_decode(L, B, C, S, q, q_stride, gate, gate_stride, gate_bias,
                                            out, out_stride, workspace,
                                            static_cast<hipStream_t>(stream)));
+}
+
+}  // namespace
+
+extern "C" {
+
+beam_status beam_attn_decode(const beam_layer_desc* layer, const beam_batch* batch,
+                             const beam_kv_cache* cache, const void* q, int64_t q_stride,
+                             const void* gate, int64_t gate_stride, const void* gate_bias,
+                             void* out, int64_t out_stride, void* workspace,
+                             size_t workspace_bytes, void* stream) {
+  return attn_decode(layer, batch, cache, q, q_stride, gate, gate_stride, gate_bias, out,
+                     out_stride, workspace, workspace_bytes, false, stream);
+}
+
+beam_status beam_attn_decode_noalloc(const beam_layer_desc* layer, const beam_batch* batch,
+                                     const beam_kv_cache* cache, const void* q, int64_t q_stride,
+                                     const void* gate, int64_t gate_stride, const void* gate_bias,
+                                     void* out, int64_t out_stride, void* stream) {
+  return attn_decode(layer, batch, cache, q, q_stride, gate, gate_stride, gate_bias, out,
+                     out_stride, nullptr, 0, true, stream);
 }
 
 beam_status beam_head_gate(const beam_layer_desc* layer, int64_t num_tokens, const void* attn,
