@@ -431,17 +431,12 @@ def run_decode(args, result, oracle_out=None):
             }
             log(f"  decode config{cfg}-{kind}: {dec[f'config{cfg}-{kind}']}")
             if oracle_out is not None:
-                # the oracle on the same bytes: in full, except the full layer of the two
-                # fp8 workloads, which runs on KV head 0 (an exact eighth of the work,
-                # heads being independent) and is scaled by 8
-                sample_head = 0 if (cfg in (3, 4) and kind == "full") else None
-                inp = host_inputs(call, range(call.num_seqs), kv_head=sample_head)
-                secs = time_oracle(inp)
-                full_s = secs * (call.num_kv_heads if sample_head is not None else 1)
+                # the oracle on the same bytes, in full
+                inp = host_inputs(call, range(call.num_seqs))
+                full_s = time_oracle(inp)
                 oracle_out[f"config{cfg}-{kind}"] = {
                     "s": round(full_s, 3), "tokens_per_s": round(sum(ql) / full_s, 3),
-                    "sample": ("KV head 0 of 8 (all rows, all keys), time x 8"
-                               if sample_head is not None else "in full"),
+                    "sample": "in full",
                     "gpu_speedup": round(full_s / ((per_d["decode"] + per_d["kvwrite"]) * 1e-3), 1)}
                 log(f"  oracle config{cfg}-{kind}: {oracle_out[f'config{cfg}-{kind}']}")
                 del inp
