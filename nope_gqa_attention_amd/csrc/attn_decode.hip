@@ -34,9 +34,14 @@
 namespace beam {
 namespace {
 
-constexpr int kVRowBytes = kHeadDim * 2 + 16;     // bf16 V row in LDS, padded
+constexpr int kVRowBytes = kHeadDim * 2 + 16;     // bf16 K or V row in LDS, padded
 constexpr int kVRowsPerWave = 32;                 // keys staged per half-page step
-constexpr int lds_bytes(int waves) { return waves * kVRowsPerWave * kVRowBytes; }
+// K goes through LDS as well in the 4-wave kernel (see fetch_k); the 12-wave kernel of
+// latency-bound launches keeps the V staging only, to fit its 12 waves in LDS.
+constexpr bool k_staged(int waves) { return waves == kDecodeWaves; }
+constexpr int lds_bytes(int waves) {
+  return waves * kVRowsPerWave * kVRowBytes * (k_staged(waves) ? 2 : 1);
+}
 // Output regions of the in-workgroup merge: the largest divisor of the wave count whose
 // regions (fp32 [rows][128], padded) fit the V staging space.
 constexpr int merge_regions(int waves, int region_bytes) {
@@ -50,10 +55,11 @@ constexpr int kBufferRsrcWord3 = 0x00020000;         // raw buffer, 32-bit data 
 constexpr int kLoadNonTemporal = 2;                  // cache-policy bit: nt
 
 // Start of the 8-value slice of head dimension used by MFMA i (0..3) in lane group g
-// (lane / 16). bf16: one 16-byte load per MFMA; fp8: one 16-byte load feeds 2 MFMAs.
-template <int KV>
+// (lane / 16). K read from LDS (always bf16 there) or straight from a bf16 cache: one
+// 16-byte piece per MFMA; straight from an fp8 cache: one 16-byte load feeds 2 MFMAs.
+template <int KV, bool KST>
 __device__ __forceinline__ int dslice(int i, int g) {
-  return KV == BEAM_KV_BF16 ? 32 * i + 8 * g : 64 * (i / 2) + 16 * g + 8 * (i % 2);
+  return (KST || KV == BEAM_KV_BF16) ? 32 * i + 8 * g : 64 * (i / 2) + 16 * g + 8 * (i % 2);
 }
 
 
@@ -82,6 +88,7 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(W == kDe
     int64_t out_stride, float* __restrict__ ws_o, float* __restrict__ ws_ml, int64_t ws_rows) {
   constexpr int kThreads = W * 64;
   constexpr int kLdsBytes = lds_bytes(W);
+  constexpr bool KST = k_staged(W);
   constexpr int kStep = W * kPage;                    // keys of one page per wave
   __shared__ __attribute__((aligned(16))) unsigned char lds[kLdsBytes];
   __shared__ float s_m[W][kDecodeMaxRowsPerChunk];
@@ -125,7 +132,7 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(W == kDe
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       u32x4_t v = {0u, 0u, 0u, 0u};
-      if (valid) v = *reinterpret_cast<const u32x4_t*>(qrow + dslice<KV>(i, lg));
+      if (valid) v = *reinterpret_cast<const u32x4_t*>(qrow + dslice<KV, KST>(i, lg));
       qop[rb][i] = __builtin_bit_cast(bf16x8_t, v);
     }
   }
@@ -145,7 +152,8 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(W == kDe
     for (int d = 0; d < 8; ++d) acc[rb][d] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   }
 
-  unsigned char* vlds = lds + wave * kVRowsPerWave * kVRowBytes;
+  unsigned char* vlds = lds + wave * kVRowsPerWave * kVRowBytes * (KST ? 2 : 1);
+  unsigned char* klds = vlds + kVRowsPerWave * kVRowBytes;     // (K staging, KST only)
 
   // This wave's pages: keys pk = k_begin + 64*(wave + W*pi), pi = 0, 1, ...; each page is
   // two half-steps of 32 keys, each loaded into one register set and then computed. The
@@ -180,20 +188,33 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(W == kDe
   constexpr int kElem = KV == BEAM_KV_BF16 ? 2 : 1;
   constexpr int kRow = kHeadDim * kElem;                  // bytes per key row
   uint32_t koff[kKRegs], voff[kVRegs];
+  // V (and staged K): every load instruction reads whole rows, 1 KiB of consecutive
+  // bytes (4 bf16 or 8 fp8 rows). K read straight into MFMA operands instead takes 16
+  // rows x 64 bytes per instruction (half cache lines), which streams about 20% slower.
   if (KV == BEAM_KV_BF16) {
 #pragma unroll
-    for (int sb = 0; sb < 2; ++sb)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) koff[4 * sb + i] = (16 * sb + lc) * kRow + dslice<KV>(i, lg) * 2;
-#pragma unroll
     for (int it = 0; it < 8; ++it) voff[it] = (lane / 16 + 4 * it) * kRow + lc * 16;
+    if (KST) {
+#pragma unroll
+      for (int it = 0; it < 8; ++it) koff[it] = voff[it];
+    } else {
+#pragma unroll
+      for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) koff[4 * sb + i] = (16 * sb + lc) * kRow + dslice<KV, KST>(i, lg) * 2;
+    }
   } else {
 #pragma unroll
-    for (int sb = 0; sb < 2; ++sb)
-#pragma unroll
-      for (int jj = 0; jj < 2; ++jj) koff[2 * sb + jj] = (16 * sb + lc) * kRow + 64 * jj + 16 * lg;
-#pragma unroll
     for (int it = 0; it < 4; ++it) voff[it] = (lane / 8 + 8 * it) * kRow + (lane % 8) * 16;
+    if (KST) {
+#pragma unroll
+      for (int it = 0; it < 4; ++it) koff[it] = voff[it];
+    } else {
+#pragma unroll
+      for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+        for (int jj = 0; jj < 2; ++jj) koff[2 * sb + jj] = (16 * sb + lc) * kRow + 64 * jj + 16 * lg;
+    }
   }
   const int64_t head_bytes = (int64_t)kPage * kRow;       // one KV head's page
   // One buffer resource per half-page: the uniform base sits in scalar registers and
@@ -229,14 +250,53 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(W == kDe
   constexpr bool kPipe = W == kDecodeWaves && decode_wgs_per_cu(RB, KV) == 2 &&
                          !(KV == BEAM_KV_BF16 && RB == 3);
 
+  // stage 32 K or V rows (row-major bf16) in this wave's LDS region: `reg` holds whole
+  // rows as loaded (see voff); fp8 codes are widened exactly to bf16 on the way
+  auto stage_rows = [&](unsigned char* dst, const u32x4_t (&reg)[kVRegs], int kk0, bool zero_tail) {
+    if (KV == BEAM_KV_BF16) {
+#pragma unroll
+      for (int it = 0; it < 8; ++it) {
+        const int r = lane / 16 + 4 * it;
+        u32x4_t w = reg[it];
+        if (zero_tail && kk0 + r >= kv) w = u32x4_t{0u, 0u, 0u, 0u};
+        *reinterpret_cast<u32x4_t*>(dst + r * kVRowBytes + lc * 16) = w;
+      }
+    } else {
+#pragma unroll
+      for (int it = 0; it < 4; ++it) {
+        const int r = lane / 8 + 8 * it;
+        const int cc = lane % 8;
+        u32x4_t w = reg[it];
+        if (zero_tail && kk0 + r >= kv) w = u32x4_t{0u, 0u, 0u, 0u};
+        *reinterpret_cast<bf16x8_t*>(dst + r * kVRowBytes + cc * 32) = fp8x8_to_bf16x8(w[0], w[1]);
+        *reinterpret_cast<bf16x8_t*>(dst + r * kVRowBytes + cc * 32 + 16) = fp8x8_to_bf16x8(w[2], w[3]);
+      }
+    }
+  };
+
   auto compute = [&](int j) {
     const int kk0 = (int)(first_pk + (int64_t)kStep * (j >> 1) + 32 * (j & 1));
+    if constexpr (KST) {
+      // K and V rows of this half-step into LDS; the registers are then free for the
+      // next half-step's loads, which fly during this step's compute. (Rows past the
+      // sequence end: V is zeroed, K may hold anything -- those scores are masked.)
+      stage_rows(klds, kreg, kk0, false);
+      stage_rows(vlds, vreg, kk0, true);
+      if (kPipe && j + 1 < n_half) { fetch_k(j + 1); fetch_v(j + 1); }
+    }
     // ---- S^T = K Q^T (32 keys = 2 score blocks of 16)
     f32x4_t sc[RB][2];
 #pragma unroll
     for (int sb = 0; sb < 2; ++sb) {
       bf16x8_t kop[4];
-      if (KV == BEAM_KV_BF16) {
+      if (KST) {
+        // MFMA layout from the staged rows: lane (lc, lg) reads row 16 sb + lc, dims
+        // 32 i + 8 lg; the 16-byte row padding puts the 16 rows of one read in distinct
+        // banks
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          kop[i] = *reinterpret_cast<const bf16x8_t*>(klds + (16 * sb + lc) * kVRowBytes + (32 * i + 8 * lg) * 2);
+      } else if (KV == BEAM_KV_BF16) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) kop[i] = __builtin_bit_cast(bf16x8_t, kreg[4 * sb + i]);
       } else {
@@ -255,29 +315,13 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(W == kDe
         sc[rb][sb] = sacc;
       }
     }
-    if (kPipe && j + 1 < n_half) fetch_k(j + 1);
-    // ---- stage V rows (row-major bf16) in this wave's LDS region; keys >= kv are
-    // zeroed so that their (zero) probabilities never meet NaN payloads
-    if (KV == BEAM_KV_BF16) {
-#pragma unroll
-      for (int it = 0; it < 8; ++it) {
-        const int r = lane / 16 + 4 * it;
-        u32x4_t w = vreg[it];
-        if (kk0 + r >= kv) w = u32x4_t{0u, 0u, 0u, 0u};
-        *reinterpret_cast<u32x4_t*>(vlds + r * kVRowBytes + lc * 16) = w;
-      }
-    } else {
-#pragma unroll
-      for (int it = 0; it < 4; ++it) {
-        const int r = lane / 8 + 8 * it;
-        const int cc = lane % 8;
-        u32x4_t w = vreg[it];
-        if (kk0 + r >= kv) w = u32x4_t{0u, 0u, 0u, 0u};
-        *reinterpret_cast<bf16x8_t*>(vlds + r * kVRowBytes + cc * 32) = fp8x8_to_bf16x8(w[0], w[1]);
-        *reinterpret_cast<bf16x8_t*>(vlds + r * kVRowBytes + cc * 32 + 16) = fp8x8_to_bf16x8(w[2], w[3]);
-      }
+    if constexpr (!KST) {
+      if (kPipe && j + 1 < n_half) fetch_k(j + 1);
+      // ---- stage V rows (row-major bf16) in this wave's LDS region; keys >= kv are
+      // zeroed so that their (zero) probabilities never meet NaN payloads
+      stage_rows(vlds, vreg, kk0, true);
+      if (kPipe && j + 1 < n_half) fetch_v(j + 1);
     }
-    if (kPipe && j + 1 < n_half) fetch_v(j + 1);
     // ---- mask, online softmax, P^T as bf16 (k-slot order: block 0 keys 4lg..4lg+3,
     // then block 1 keys 16+4lg..)
     const bool need_mask = (kk0 + 31 > all_hi) || (kk0 < all_lo);

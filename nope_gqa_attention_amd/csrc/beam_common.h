@@ -58,12 +58,12 @@ constexpr int kDecodeWideWaves = 12;
 constexpr int kDecodeKeysPerBlockStep = kDecodeWaves * kPage;  // one page per wave per step
 constexpr int kDecodeMaxRowsPerChunk = 48;
 constexpr int kDecodeMaxSplits = 2048;                // bound of the merge kernel's weight table
-// Decode split-kernel workgroups (of 4 waves) resident per CU that its register budget is
-// built for, i.e. waves per SIMD: 3 for one 16-row block over an fp8 cache (loads hidden by
-// residency), 2 otherwise (bf16 with one block streams with its next loads in flight,
-// which needs the registers of the third wave). LDS (36 KiB per workgroup) admits 4.
+// Decode split-kernel workgroups (of 4 waves) resident per CU that its register and LDS
+// budgets are built for, i.e. waves per SIMD: 2. Each wave streams with its next
+// half-step's loads in flight, and stages K and V rows in 17 KiB of LDS (70 KiB per
+// workgroup), which admits 2 workgroups per CU.
 constexpr int decode_wgs_per_cu(int row_blocks, int kv_dtype) {
-  return (row_blocks == 1 && kv_dtype == BEAM_KV_FP8_E4M3) ? 3 : 2;
+  return (void)row_blocks, (void)kv_dtype, 2;
 }
 
 hipError_t launch_qknorm_kvwrite(const LayerParams& L, const BatchParams& B, const CacheParams& C,
