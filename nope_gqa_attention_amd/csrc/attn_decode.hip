@@ -63,15 +63,6 @@ __device__ __forceinline__ int dslice(int i, int g) {
 }
 
 
-__device__ __forceinline__ int seq_of_token(const int32_t* q_start, int num_seqs, int64_t t) {
-  int lo = 0, hi = num_seqs - 1;
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    if ((int64_t)q_start[mid] <= t) lo = mid; else hi = mid - 1;
-  }
-  return lo;
-}
-
 // First key of the sequence's visited range, rounded down to a page.
 __device__ __forceinline__ int64_t range_base(const LayerParams& L, int64_t kv, int64_t n) {
   const int64_t first_pos = kv - n;
@@ -112,7 +103,20 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(W == kDe
   if (row0 >= rows_b) return;
   const int64_t base = range_base(L, kv, n);
   const int64_t k_begin = base + (int64_t)split * S.keys_per_split;
-  if (k_begin >= kv) return;
+  if (k_begin >= kv) {
+    // a split past this sequence's keys: its rows get an empty partial (max -inf, sum
+    // 0), so that the merge can weigh every split of the launch without reading the
+    // batch metadata
+    if (S.num_splits > 1) {
+      for (int i = threadIdx.x; i < S.rows_per_chunk; i += kThreads) {
+        const int64_t r = row0 + i;
+        if (r >= rows_b) break;
+        const int64_t wrow = (int64_t)split * ws_rows + (q0 + r / L.G) * L.Hq + g * L.G + r % L.G;
+        *reinterpret_cast<float2*>(ws_ml + wrow * 2) = make_float2(-INFINITY, 0.f);
+      }
+    }
+    return;
+  }
   const int64_t k_end = k_begin + S.keys_per_split < kv ? k_begin + S.keys_per_split : kv;
   const int64_t first_pos = kv - n;
 
@@ -509,10 +513,9 @@ __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(
   const int h = (int)(row % L.Hq);
   const int t = threadIdx.x, wave = t / 64, lane = t % 64;
   const int q4 = t % 32, grp = t / 32;
-  // ---- issue first, before the batch metadata arrives: this row's gate values, this
-  // thread's first (m, l) pair and its first chunk of partial outputs, for every split the
-  // launch has (the workspace holds them all; splits this row's sequence did not use are
-  // read but never weighed)
+  // ---- issue everything first: this row's gate values, this thread's first (m, l)
+  // pair and its first chunk of partial outputs, for every split the launch has (splits
+  // past this row's sequence hold an empty pair, weight 0)
   u32x2_t gw = {0u, 0u};
   if (gate != nullptr && t < 32) gw = *reinterpret_cast<const u32x2_t*>(gate + tok * gate_stride + (int64_t)h * kHeadDim + 4 * q4);
   // (rows past the workspace's are padding rows: they read nothing and return below)
@@ -526,56 +529,71 @@ __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(
     ov[u] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     if (sp < nsp) ov[u] = *reinterpret_cast<const f32x4_t*>(ws_o + ((int64_t)sp * ws_rows + row) * kHeadDim + 4 * q4);
   }
-  if (tok >= B.q_start[B.num_seqs]) return;      // padding row past the last sequence
-  const int b = seq_of_token(B.q_start, B.num_seqs, tok);
-  const int64_t n = (int64_t)B.q_start[b + 1] - B.q_start[b];
-  const int64_t kv = B.kv_len[b];
-  const int64_t base = range_base(L, kv, n);
-  const int used = (int)((kv - base + S.keys_per_split - 1) / S.keys_per_split);
-  if (t >= used) ml0 = make_float2(-INFINITY, 0.f);
-  // ---- global max of the split maxima
+  // padding rows past the last sequence get no output (the test sits before the output
+  // write only, so its load overlaps the others)
+  const bool padding = tok >= B.q_start[B.num_seqs];
+  // ---- global max of the split maxima. Every split of the launch has a pair for this
+  // row: splits past the sequence's keys wrote (-inf, 0).
   float M = ml0.x;
-  for (int sp = t + kMergeThreads; sp < used; sp += kMergeThreads)
+  for (int sp = t + kMergeThreads; sp < nsp; sp += kMergeThreads)
     M = fmaxf(M, ws_ml[((int64_t)sp * ws_rows + row) * 2]);
-  M = wave_xor_max(M, 1); M = wave_xor_max(M, 2); M = wave_xor_max(M, 4);
-  M = wave_xor_max(M, 8); M = wave_xor_max(M, 16); M = wave_xor_max(M, 32);
-  if (lane == 0) s_red[wave] = M;
-  __syncthreads();
-  M = fmaxf(fmaxf(s_red[0], s_red[1]), fmaxf(s_red[2], s_red[3]));
-  __syncthreads();                                 // s_red is reused for the sum below
-  // ---- split weights (LDS) and the weighted sum of the l's
   float lsum = 0.f;
-  for (int sp = t; sp < used; sp += kMergeThreads) {
-    const float2 ml = sp == t ? ml0 : *reinterpret_cast<const float2*>(ws_ml + ((int64_t)sp * ws_rows + row) * 2);
-    const float w = ml.x == -INFINITY ? 0.f : exp2f(ml.x - M);
-    s_w[sp] = w;
-    lsum += w * ml.y;
-  }
+  if (nsp <= 64) {
+    // one wave holds every pair: reduce without the workgroup
+    if (wave == 0) {
+      M = wave_xor_max(M, 1); M = wave_xor_max(M, 2); M = wave_xor_max(M, 4);
+      M = wave_xor_max(M, 8); M = wave_xor_max(M, 16); M = wave_xor_max(M, 32);
+      const float w = ml0.x == -INFINITY ? 0.f : exp2f(ml0.x - M);
+      if (t < nsp) s_w[t] = w;
+      lsum = w * ml0.y;
 #pragma unroll
-  for (int o = 1; o < 64; o <<= 1) lsum += __shfl_xor(lsum, o, 64);
-  if (lane == 0) s_red[wave] = lsum;
-  __syncthreads();
-  const float ltot = ((s_red[0] + s_red[1]) + s_red[2]) + s_red[3];
-  // ---- weighted partial outputs, chunk by chunk
+      for (int o = 1; o < 64; o <<= 1) lsum += __shfl_xor(lsum, o, 64);
+      if (lane == 0) s_red[0] = lsum;
+    }
+    __syncthreads();
+    lsum = s_red[0];
+  } else {
+    M = wave_xor_max(M, 1); M = wave_xor_max(M, 2); M = wave_xor_max(M, 4);
+    M = wave_xor_max(M, 8); M = wave_xor_max(M, 16); M = wave_xor_max(M, 32);
+    if (lane == 0) s_red[wave] = M;
+    __syncthreads();
+    M = fmaxf(fmaxf(s_red[0], s_red[1]), fmaxf(s_red[2], s_red[3]));
+    __syncthreads();                                 // s_red is reused for the sum below
+    // ---- split weights (LDS) and the weighted sum of the l's
+    for (int sp = t; sp < nsp; sp += kMergeThreads) {
+      const float2 ml = sp == t ? ml0 : *reinterpret_cast<const float2*>(ws_ml + ((int64_t)sp * ws_rows + row) * 2);
+      const float w = ml.x == -INFINITY ? 0.f : exp2f(ml.x - M);
+      s_w[sp] = w;
+      lsum += w * ml.y;
+    }
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) lsum += __shfl_xor(lsum, o, 64);
+    if (lane == 0) s_red[wave] = lsum;
+    __syncthreads();
+    lsum = ((s_red[0] + s_red[1]) + s_red[2]) + s_red[3];
+  }
+  const float ltot = lsum;
+  // ---- weighted partial outputs, chunk by chunk (a split of weight 0 -- empty, or no
+  // visible key for this row -- is skipped: its partial output may hold anything)
   f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-  for (int c0 = 0; c0 < used; c0 += kMergeChunk) {
+  for (int c0 = 0; c0 < nsp; c0 += kMergeChunk) {
     if (c0 > 0) {
 #pragma unroll
       for (int u = 0; u < kMergeUnroll; ++u) {
         const int sp = c0 + grp + kMergeGroups * u;
         ov[u] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-        if (sp < used) ov[u] = *reinterpret_cast<const f32x4_t*>(ws_o + ((int64_t)sp * ws_rows + row) * kHeadDim + 4 * q4);
+        if (sp < nsp) ov[u] = *reinterpret_cast<const f32x4_t*>(ws_o + ((int64_t)sp * ws_rows + row) * kHeadDim + 4 * q4);
       }
     }
 #pragma unroll
     for (int u = 0; u < kMergeUnroll; ++u) {
       const int sp = c0 + grp + kMergeGroups * u;
-      if (sp < used) acc += s_w[sp] * ov[u];
+      if (sp < nsp && s_w[sp] != 0.f) acc += s_w[sp] * ov[u];
     }
   }
   s_acc[grp][q4] = acc;
   __syncthreads();
-  if (t >= 32) return;
+  if (t >= 32 || padding) return;
   f32x4_t y = s_acc[0][q4];
 #pragma unroll
   for (int gi = 1; gi < kMergeGroups; ++gi) y += s_acc[gi][q4];
