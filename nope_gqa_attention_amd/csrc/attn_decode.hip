@@ -63,6 +63,28 @@ __device__ __forceinline__ int dslice(int i, int g) {
 }
 
 
+// Max / sum over lanes l, l^16, l^32, l^48 (the four lane groups that hold one row's
+// scores) with the gfx950 lane-row swaps: plain VALU instructions, where a shuffle
+// through LDS (ds_bpermute) would put an LDS round trip on the softmax's critical path.
+// Each swap returns two values whose elementwise max (or sum) combines lane l with
+// lane l^16 (resp. l^32), whichever rows the instruction exchanged.
+__device__ __forceinline__ float max_over_lane_groups(float x) {
+  const uint32_t u = __float_as_uint(x);
+  const auto a = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  const float m = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const uint32_t v = __float_as_uint(m);
+  const auto b = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float sum_over_lane_groups(float x) {
+  const uint32_t u = __float_as_uint(x);
+  const auto a = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  const float m = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const uint32_t v = __float_as_uint(m);
+  const auto b = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
 // First key of the sequence's visited range, rounded down to a page.
 __device__ __forceinline__ int64_t range_base(const LayerParams& L, int64_t kv, int64_t n) {
   const int64_t first_pos = kv - n;
@@ -285,7 +307,8 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(W == kDe
       // next half-step's loads, which fly during this step's compute. (Rows past the
       // sequence end: V is zeroed, K may hold anything -- those scores are masked.)
       stage_rows(klds, kreg, kk0, false);
-      stage_rows(vlds, vreg, kk0, true);
+      if (kk0 + 32 > kv) stage_rows(vlds, vreg, kk0, true);   // (the sequence's last keys)
+      else stage_rows(vlds, vreg, kk0, false);
       if (kPipe && j + 1 < n_half) { fetch_k(j + 1); fetch_v(j + 1); }
     }
     // ---- S^T = K Q^T (32 keys = 2 score blocks of 16)
@@ -323,7 +346,8 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(W == kDe
       if (kPipe && j + 1 < n_half) fetch_k(j + 1);
       // ---- stage V rows (row-major bf16) in this wave's LDS region; keys >= kv are
       // zeroed so that their (zero) probabilities never meet NaN payloads
-      stage_rows(vlds, vreg, kk0, true);
+      if (kk0 + 32 > kv) stage_rows(vlds, vreg, kk0, true);
+      else stage_rows(vlds, vreg, kk0, false);
       if (kPipe && j + 1 < n_half) fetch_v(j + 1);
     }
     // ---- mask, online softmax, P^T as bf16 (k-slot order: block 0 keys 4lg..4lg+3,
@@ -349,8 +373,7 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(W == kDe
       float mx = sv[0];
 #pragma unroll
       for (int e = 1; e < 8; ++e) mx = fmaxf(mx, sv[e]);
-      mx = wave_xor_max(mx, 16);
-      mx = wave_xor_max(mx, 32);
+      mx = max_over_lane_groups(mx);
       mx *= c;
       // raise the running max only when some row's maximum grew by more than 2^8 (log2
       // domain): the rescale of the output is then skipped on almost every step, and the
@@ -407,8 +430,7 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(W == kDe
   // ---- merge the waves of this workgroup (LDS), then write
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) {
-    l_run[rb] += __shfl_xor(l_run[rb], 16, 64);
-    l_run[rb] += __shfl_xor(l_run[rb], 32, 64);
+    l_run[rb] = sum_over_lane_groups(l_run[rb]);
     if (lg == 0) {
       s_m[wave][16 * rb + lc] = m_run[rb];
       s_l[wave][16 * rb + lc] = l_run[rb];
