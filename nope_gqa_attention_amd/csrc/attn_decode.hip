@@ -387,15 +387,19 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(W == kDe
         m_run[rb] = m_new;
       }
       const float m_use = m_run[rb] == -INFINITY ? 0.f : m_run[rb];
-      float psum = 0.f;
       bf16x8_t pb;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float pe = __builtin_amdgcn_exp2f(fmaf(sv[e], c, -m_use));
-        psum += pe;
-        pb[e] = (__bf16)pe;
+      for (int e = 0; e < 8; ++e) pb[e] = (__bf16)__builtin_amdgcn_exp2f(fmaf(sv[e], c, -m_use));
+      // the row sum adds the bf16-rounded weights that P V multiplies, two per
+      // instruction (v_dot2_f32_bf16 against ones, fp32 accumulation)
+      float ls = l_run[rb];
+#pragma unroll
+      for (int e = 0; e < 8; e += 2) {
+        const bf16x2_t pair = {pb[e], pb[e + 1]};
+        const bf16x2_t one = {(__bf16)1.0f, (__bf16)1.0f};
+        ls = __builtin_amdgcn_fdot2_f32_bf16(pair, one, ls, false);
       }
-      l_run[rb] += psum;
+      l_run[rb] = ls;
       pop[rb] = pb;
     }
     // ---- O^T += V^T P^T, V^T via transposing LDS reads
