@@ -8,6 +8,7 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
 #include <mutex>
 
@@ -47,12 +48,32 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 //    workgroups per CU sized for the longest (measured best on a 32-sequence batch of
 //    8K..128K keys); workgroups past a shorter sequence's end exit at once and the
 //    dispatcher balances the rest.
-int decode_cu_count() {
+int device_cu_count() {
   int dev = 0, cus = 0;
   if (hipGetDevice(&dev) != hipSuccess ||
       hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
     cus = 256;
   return cus;
+}
+
+// Prefill key split (full layers): one prefill workgroup runs per CU at a time (its
+// registers and LDS), so an XCD's share of the row tiles runs in rounds of one tile per
+// CU. Halving a row tile and giving each half of its key tiles to one of two 4-wave
+// streams gives two workgroups of about 0.58 of the time each (the second stream's own
+// tile copies and the merge cost the rest). Mode 2 splits the tiles of an XCD's last
+// round when that round would leave at least half of its CUs idle: 384 row tiles on 256
+// CUs (2 rounds, the second half empty) run 256 whole tiles, then 256 split halves, and
+// a grid of a few dozen tiles runs all split. Contexts under 1,024 keys keep whole
+// ranges: a workgroup's fixed costs would dominate its half.
+// BEAMATTN_PREFILL_KEY_SPLIT=0 (never) or 1 (every row tile) in the environment overrides
+// the choice.
+int choose_prefill_split_mode(const beam::LayerParams& L, const beam::BatchParams& B) {
+  if (L.kind != BEAM_LAYER_FULL) return 0;
+  if (const char* e = getenv("BEAMATTN_PREFILL_KEY_SPLIT")) {
+    if (e[0] == '0') return 0;
+    if (e[0] == '1') return 1;
+  }
+  return B.max_kv_len < 1024 ? 0 : 2;
 }
 
 beam::DecodeSplit choose_decode_split(int32_t G, int32_t kind, int32_t window, int32_t num_seqs,
@@ -80,7 +101,7 @@ beam::DecodeSplit choose_decode_split(int32_t G, int32_t kind, int32_t window, i
   }
   if (range < 1) range = 1;
   const int64_t unit = (int64_t)num_seqs * Hkv * s.row_chunks;   // workgroups per split index
-  const int64_t slots = (int64_t)decode_cu_count() * beam::decode_wgs_per_cu(s.rows_per_chunk / 16, kv_dtype);
+  const int64_t slots = (int64_t)device_cu_count() * beam::decode_wgs_per_cu(s.rows_per_chunk / 16, kv_dtype);
   const int64_t step = beam::kDecodeKeysPerBlockStep;
   const int64_t rows_in_chunk = rows < s.rows_per_chunk ? rows : s.rows_per_chunk;
   int64_t min_keys = rows_in_chunk * (beam::kHeadDim + 2) * 4 * 64 / 256;
@@ -91,7 +112,7 @@ beam::DecodeSplit choose_decode_split(int32_t G, int32_t kind, int32_t window, i
   // batch-1 decode 24.3 -> 19.2 us, the 8-token 1M verify 110 -> 72 us).
   // (a range that fits one split at that length stays one split: no merge launch)
   if (num_seqs == 1 && range > min_keys &&
-      unit * ((range + min_keys - 1) / min_keys) < decode_cu_count() && min_keys > 2 * step)
+      unit * ((range + min_keys - 1) / min_keys) < device_cu_count() && min_keys > 2 * step)
     min_keys = 2 * step;
   const int64_t max_keys = ((range + step - 1) / step) * step;
   if (min_keys > max_keys) min_keys = max_keys;
@@ -104,7 +125,7 @@ beam::DecodeSplit choose_decode_split(int32_t G, int32_t kind, int32_t window, i
       if (best < 0.0 || cost < best) { best = cost; kps = k; }
     }
   } else {
-    const int64_t target = 32 * (int64_t)decode_cu_count();
+    const int64_t target = 32 * (int64_t)device_cu_count();
     const int64_t want = (target + unit - 1) / unit;                 // splits per sequence
     kps = (range + want - 1) / want;
     kps = ((kps + step - 1) / step) * step;
@@ -121,7 +142,7 @@ beam::DecodeSplit choose_decode_split(int32_t G, int32_t kind, int32_t window, i
   // two or three 16-row blocks through every step. Re-read bytes are what this trades,
   // so it applies only while the workgroups are fewer than the CUs.
   if (s.num_splits == 1 && s.rows_per_chunk > 16 &&
-      (int64_t)num_seqs * Hkv * s.row_chunks < decode_cu_count()) {
+      (int64_t)num_seqs * Hkv * s.row_chunks < device_cu_count()) {
     s.row_chunks = (int32_t)((rows + 15) / 16);
     s.rows_per_chunk = 16;
   }
@@ -131,7 +152,7 @@ beam::DecodeSplit choose_decode_split(int32_t G, int32_t kind, int32_t window, i
   // fewer workgroups (batch-1) the fixed costs dominate and 4 waves were slightly faster.
   const int64_t wgs = (int64_t)num_seqs * Hkv * s.row_chunks;
   s.waves = beam::kDecodeWaves;
-  if (s.num_splits == 1 && s.rows_per_chunk == 16 && wgs >= 16 && wgs <= decode_cu_count())
+  if (s.num_splits == 1 && s.rows_per_chunk == 16 && wgs >= 16 && wgs <= device_cu_count())
     s.waves = beam::kDecodeWideWaves;
   return s;
 }
@@ -371,9 +392,17 @@ beam_status beam_attn_prefill(const beam_layer_desc* layer, const beam_batch* ba
   if ((s = check_gate(gate, gate_stride, gate_bias, L.Hq, N)) != BEAM_OK) return s;
   if ((int64_t)B.max_q_len * L.G > 0x7FFFFFFF)
     return fail(BEAM_ERR_INVALID_ARG, "max_q_len * query heads per KV head must fit in int32");
+  {
+    const int64_t rpb = beam::prefill_rows_per_block(L.kind, false);
+    const int64_t tiles = ((int64_t)B.max_q_len * L.G + rpb - 1) / rpb;
+    if (tiles * L.Hkv * B.num_seqs > 0x3FFFFFFF)
+      return fail(BEAM_ERR_INVALID_ARG, "prefill row tiles x KV heads x sequences must be at most 2^30");
+  }
   BEAM_DEBUG_CHECK_BATCH(L, B, C, stream);
-  return launched(beam::launch_attn_prefill(L, B, C, q, q_stride, gate, gate_stride, gate_bias,
-                                            out, out_stride, static_cast<hipStream_t>(stream)));
+  return launched(beam::launch_attn_prefill(L, B, C, choose_prefill_split_mode(L, B),
+                                            device_cu_count(), q, q_stride, gate, gate_stride,
+                                            gate_bias, out, out_stride,
+                                            static_cast<hipStream_t>(stream)));
 }
 
 size_t beam_attn_decode_workspace_bytes(const beam_layer_desc* layer, int32_t num_seqs,

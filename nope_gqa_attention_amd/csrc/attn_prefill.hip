@@ -44,10 +44,10 @@
 namespace beam {
 namespace {
 
-// Workgroup shape: waves x one 32-row MFMA block each; 8 waves (256 rows) for full
-// layers, 4 (128 rows) for sliding ones. Both keep 2 waves per SIMD (at most 256 VGPRs).
+// Workgroup shape (prefill_waves, prefill_rows_per_block): waves x one 32-row MFMA block
+// each; 8 waves (256 rows) for full layers, 4 (128 rows) for sliding ones, 8 over 128 rows
+// with the key split. All keep 2 waves per SIMD (at most 256 VGPRs).
 constexpr int kRowsPerWave = 32;
-constexpr int prefill_waves(int kind) { return kind == BEAM_LAYER_SWA ? 4 : 8; }
 constexpr int kRowBytes = kHeadDim * 2;                  // 256-byte bf16 row, swizzled chunks
 constexpr int kTileBytes = kPage * kRowBytes;            // one K or V page tile: 16 KiB
 constexpr float kLog2e = 1.4426950408889634f;
@@ -117,32 +117,64 @@ __device__ __forceinline__ float swap_halves_sum(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-// Launch bound: the larger workgroup (512 threads), which also caps both shapes at 256
-// VGPRs, i.e. 2 waves per SIMD.
-template <int KIND, int KV>
-__global__ __launch_bounds__(512) void prefill_kernel(
-    LayerParams L, BatchParams B, CacheParams C, const uint16_t* __restrict__ q, int64_t q_stride,
-    const uint16_t* __restrict__ gate, int64_t gate_stride, const uint16_t* __restrict__ gate_bias,
-    uint16_t* out, int64_t out_stride) {
-  constexpr int kWaves = prefill_waves(KIND);
-  constexpr int kThreads = kWaves * 64;
-  constexpr int kRowsPerBlock = kWaves * kRowsPerWave;
-  __shared__ __attribute__((aligned(1024))) unsigned char lds[2 * 2 * kTileBytes];
+// Work list of a launch: `units` row tiles of the full height (prefill_rows_per_block
+// without the split), ordered (sequence, KV head, tile). Blocks are dispatched
+// round-robin over the 8 XCDs (each with its own L2), so block `lin` runs on XCD lin % 8;
+// each XCD takes a contiguous range of the list, in which the row tiles of one (sequence,
+// KV head) are consecutive, so that the blocks streaming the same K/V pages share an L2.
+// Full layers may run some units as two blocks of half the rows with the key range split
+// between two wave streams (prefill_rows, SPLIT): split_mode 1 splits every unit; 2 splits
+// the units of an XCD's last round when that round would leave at least half of the XCD's
+// CUs idle (one prefill block runs per CU at a time), so that it runs twice as many
+// blocks of about half the length.
+struct PrefillGrid {
+  int32_t units;
+  int32_t tiles;           // row tiles per (sequence, KV head)
+  int32_t split_mode;      // 0 none, 1 all, 2 the last round where it is at most half full
+  int32_t cus_per_xcd;
+};
 
-  // Blocks are dispatched round-robin over the 8 XCDs (each with its own L2). Remap the
-  // linear block id so that each XCD runs a contiguous range of the work list, in which
-  // the row tiles of one (sequence, KV head) are consecutive: the blocks that stream the
-  // same K/V pages then share one L2.
-  const int num_blocks = gridDim.x * gridDim.y * gridDim.z;
-  const int lin = blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z);
-  const int xcd = lin % kNumXcds, slot = lin / kNumXcds;
-  const int per = num_blocks / kNumXcds, extra = num_blocks % kNumXcds;
-  const int work = xcd * per + min(xcd, extra) + slot;
-  const int tile = work % gridDim.x;
-  const int g = (work / gridDim.x) % gridDim.y;
-  const int b = work / (gridDim.x * gridDim.y);
+// Units of XCD `xcd`: n of them from `base`, of which the last n_split run split.
+__host__ __device__ inline void prefill_xcd_plan(const PrefillGrid& P, int xcd, int* n, int* base,
+                                                 int* n_split) {
+  const int per = P.units / kNumXcds, extra = P.units % kNumXcds;
+  *n = per + (xcd < extra ? 1 : 0);
+  *base = xcd * per + (xcd < extra ? xcd : extra);
+  *n_split = 0;
+  if (P.split_mode == 1) {
+    *n_split = *n;
+  } else if (P.split_mode == 2 && *n > 0) {
+    const int rounds = (*n + P.cus_per_xcd - 1) / P.cus_per_xcd;
+    const int last = *n - (rounds - 1) * P.cus_per_xcd;
+    if (2 * last <= P.cus_per_xcd) *n_split = last;
+  }
+}
+
+// One row tile: rows [tile_row0, tile_row0 + rows per block) of the (token, query head)
+// rows of KV head g of sequence b. `lds` is the kernel's LDS array.
+//
+// SPLIT (full layers): the workgroup's 8 waves form two streams of 4 over the same 128
+// rows; the first walks the first half of the key tiles, the second the rest, each with
+// its own double-buffered tiles, and the second hands its (max, sum, output) to the first
+// through LDS at the end, where they combine as two partial softmaxes do.
+template <int KIND, int KV, bool SPLIT>
+__device__ __forceinline__ void prefill_rows(
+    const LayerParams& L, const BatchParams& B, const CacheParams& C, const uint16_t* __restrict__ q,
+    int64_t q_stride, const uint16_t* __restrict__ gate, int64_t gate_stride,
+    const uint16_t* __restrict__ gate_bias, uint16_t* out, int64_t out_stride, int tile_row0,
+    int g, int b, unsigned char* lds) {
+  constexpr int kWaves = prefill_waves(KIND);
+  constexpr int kStreams = SPLIT ? 2 : 1;                // key-range streams per workgroup
+  constexpr int kStreamWaves = kWaves / kStreams;        // waves sharing one tile stream
+  constexpr int kStreamThreads = kStreamWaves * 64;
+  constexpr int kRowsPerBlock = kStreamWaves * kRowsPerWave;
+  constexpr int kStreamLds = 2 * 2 * kTileBytes;         // two buffers of one K and one V tile
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid / 64);   // uniform: kept in a scalar register
+  const int kstream = SPLIT ? wave / kStreamWaves : 0;   // 1: the second key half
+  const int rwave = SPLIT ? wave % kStreamWaves : wave;  // this wave's 32-row block of the tile
+  const int stid = SPLIT ? tid % kStreamThreads : tid;   // thread index among its stream's waves
+  const int lds_base = kstream * kStreamLds;   // this stream's tile buffers
   const int lane = tid % 64;
   const int half = lane / 32;      // which 8-slice of each 16-wide k step this lane feeds
   const int lr = lane % 32;        // the row (within a 32-row block) this lane owns
@@ -151,7 +183,6 @@ __global__ __launch_bounds__(512) void prefill_kernel(
   const int q0 = B.q_start[b];
   const int n = B.q_start[b + 1] - q0;
   const int rows_b = n * L.G;
-  const int tile_row0 = tile * kRowsPerBlock;
   if (n <= 0 || tile_row0 >= rows_b) return;
   const int kv = B.kv_len[b];
   const int first_pos = kv - n;
@@ -163,9 +194,14 @@ __global__ __launch_bounds__(512) void prefill_kernel(
   const int key_lo = swa ? max(pos_first - L.window + 1, 0) : 0;
   const int kt_begin = key_lo / kPage;
   const int kt_end = pos_last / kPage + 1;               // exclusive
+  // this wave's stream: all of them, or (SPLIT) the first or second half, the second
+  // taking the odd one out
+  const int kt_mid = kt_begin + (kt_end - kt_begin) / 2;
+  const int s_begin = kstream == 1 ? kt_mid : kt_begin;
+  const int s_end = (SPLIT && kstream == 0) ? kt_mid : kt_end;
 
   // rows of this wave
-  const int wrow0 = tile_row0 + wave * kRowsPerWave;
+  const int wrow0 = tile_row0 + rwave * kRowsPerWave;
   const int wrows = min(tile_row0 + tile_rows - wrow0, kRowsPerWave);   // may be <= 0
   const bool wave_active = wrows > 0;
   const int w_min_pos = wave_active ? first_pos + wrow0 / L.G : 0;
@@ -214,26 +250,27 @@ __global__ __launch_bounds__(512) void prefill_kernel(
   const uint32_t lds_addr = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) unsigned char*)lds;
   int k_off[8];                       // K operand: row lr (+32 per half), chunk 2i + half
 #pragma unroll
-  for (int i = 0; i < 8; ++i) k_off[i] = lr * kRowBytes + (((2 * i + half) ^ swz_key(lr)) << 4);
+  for (int i = 0; i < 8; ++i) k_off[i] = lds_base + lr * kRowBytes + (((2 * i + half) ^ swz_key(lr)) << 4);
   // V operand, transposing reads: rows rv (+8) of each 16-key step, columns
   // 32*db + 16*(grp%2) + 4*(gi%4) = chunk 4*db + cv, byte 8*(gi%2) inside the chunk
   const int rv = 4 * (grp / 2) + gi / 4, cv = 2 * (grp % 2) + (gi % 4) / 2;
   int v_off0[4], v_off1[4];
 #pragma unroll
   for (int db = 0; db < 4; ++db) {
-    v_off0[db] = rv * kRowBytes + (((4 * db + cv) ^ swz_key(rv)) << 4) + 8 * (gi % 2);
-    v_off1[db] = (rv + 8) * kRowBytes + (((4 * db + cv) ^ swz_key(rv + 8)) << 4) + 8 * (gi % 2);
+    v_off0[db] = lds_base + rv * kRowBytes + (((4 * db + cv) ^ swz_key(rv)) << 4) + 8 * (gi % 2);
+    v_off1[db] = lds_base + (rv + 8) * kRowBytes + (((4 * db + cv) ^ swz_key(rv + 8)) << 4) + 8 * (gi % 2);
   }
 
-  // ---- direct global -> LDS copy of one K and one V page tile. Wave w copies rows
-  // [Rw, Rw + R) of each, R = 64 / waves, with R / 4 instructions per tensor; an instruction moves 64 lanes x
-  // 16 bytes = 4 rows into one contiguous 1 KiB block: lane l lands at row 4i + l/16,
-  // chunk slot l%16, so it fetches that row's chunk (l%16) ^ swz_key(row).
-  constexpr int kRowsCopied = kPage / kWaves;
+  // ---- direct global -> LDS copy of one K and one V page tile. Wave w of a stream
+  // copies rows [Rw, Rw + R) of each, R = 64 / (waves of the stream), with R / 4
+  // instructions per tensor; an instruction moves 64 lanes x 16 bytes = 4 rows into one
+  // contiguous 1 KiB block: lane l lands at row 4i + l/16, chunk slot l%16, so it fetches
+  // that row's chunk (l%16) ^ swz_key(row).
+  constexpr int kRowsCopied = kPage / kStreamWaves;
   uint32_t cp_off[kRowsCopied / 4];
 #pragma unroll
   for (int i = 0; i < kRowsCopied / 4; ++i) {
-    const int row = kRowsCopied * wave + 4 * i + lane / 16;
+    const int row = kRowsCopied * rwave + 4 * i + lane / 16;
     cp_off[i] = row * kRowBytes + (((lane % 16) ^ swz_key(row)) << 4);
   }
   // Physical pages come through scalar loads: the block table is read-only for the
@@ -241,20 +278,20 @@ __global__ __launch_bounds__(512) void prefill_kernel(
   // load per tile issued a tile ahead of its use.
   typedef __attribute__((address_space(4))) const int32_t const_i32_t;
   const_i32_t* bt_row = (const_i32_t*)(B.block_table + (int64_t)b * B.max_pages);
-  int page_ahead = bt_row[kt_begin];
+  int page_ahead = bt_row[s_begin];      // s_begin < kt_end: a page of the sequence
   constexpr int kSrcTileBytes = fp8 ? kTileBytes / 2 : kTileBytes;   // one head's page in the cache
   const int64_t head_off = (int64_t)g * kSrcTileBytes;
   const int64_t page_bytes = (int64_t)L.Hkv * kSrcTileBytes;
-  constexpr int kFp8Reps = kPage * 8 / kThreads;     // fp8 rows staged per thread
+  constexpr int kFp8Reps = kPage * 8 / kStreamThreads;   // fp8 rows staged per thread
   u32x4_t k_stage[kFp8Reps], v_stage[kFp8Reps];
 #pragma unroll
   for (int r = 0; r < kFp8Reps; ++r) { k_stage[r] = u32x4_t{0u, 0u, 0u, 0u}; v_stage[r] = k_stage[r]; }
-  const int fp8_off = (tid / 8) * kHeadDim + (tid % 8) * 16;   // byte offset in an fp8 page tile
+  const int fp8_off = (stid / 8) * kHeadDim + (stid % 8) * 16;   // byte offset in an fp8 page tile
   auto issue_tile = [&](int kt, auto buf_c) {
     constexpr int BUF = decltype(buf_c)::value;
     // page_ahead holds tile kt's page (loaded one issue earlier); fetch the next one
     const int page = page_ahead;
-    page_ahead = bt_row[kt + 1 < kt_end ? kt + 1 : kt];
+    page_ahead = bt_row[kt + 1 < s_end ? kt + 1 : kt];
     const int64_t base = (int64_t)page * page_bytes + head_off;
     const char* kb = static_cast<const char*>(C.k) + base;
     const char* vb = static_cast<const char*>(C.v) + base;
@@ -262,18 +299,18 @@ __global__ __launch_bounds__(512) void prefill_kernel(
       const __amdgpu_buffer_rsrc_t rk = tile_rsrc(kb, kTileBytes), rv = tile_rsrc(vb, kTileBytes);
 #pragma unroll
       for (int i = 0; i < kRowsCopied / 4; ++i) {
-        const int dst = BUF * 2 * kTileBytes + (kRowsCopied * wave + 4 * i) * kRowBytes;
+        const int dst = lds_base + BUF * 2 * kTileBytes + (kRowsCopied * rwave + 4 * i) * kRowBytes;
         copy16_to_lds(rk, cp_off[i], (lds_void_t*)(lds + dst));
         copy16_to_lds(rv, cp_off[i], (lds_void_t*)(lds + dst + kTileBytes));
       }
     } else {
-      // thread tid loads 16 codes (bytes 16 * (tid % 8) ..) of fp8 rows tid / 8 (+ the
-      // thread count / 8) of each tensor into registers; store_staged converts and
-      // writes them after this tile
+      // thread stid of the stream loads 16 codes (bytes 16 * (stid % 8) ..) of fp8 rows
+      // stid / 8 (+ the stream's thread count / 8) of each tensor into registers;
+      // store_staged converts and writes them after this tile
 #pragma unroll
       for (int r = 0; r < kFp8Reps; ++r) {
-        k_stage[r] = *reinterpret_cast<const u32x4_t*>(kb + fp8_off + r * (kThreads / 8) * kHeadDim);
-        v_stage[r] = *reinterpret_cast<const u32x4_t*>(vb + fp8_off + r * (kThreads / 8) * kHeadDim);
+        k_stage[r] = *reinterpret_cast<const u32x4_t*>(kb + fp8_off + r * (kStreamThreads / 8) * kHeadDim);
+        v_stage[r] = *reinterpret_cast<const u32x4_t*>(vb + fp8_off + r * (kStreamThreads / 8) * kHeadDim);
       }
     }
   };
@@ -282,10 +319,10 @@ __global__ __launch_bounds__(512) void prefill_kernel(
   auto store_staged = [&](auto buf_c) {
     if constexpr (fp8) {
       constexpr int BUF = decltype(buf_c)::value;
-      unsigned char* kt_lds = lds + BUF * 2 * kTileBytes;
+      unsigned char* kt_lds = lds + lds_base + BUF * 2 * kTileBytes;
 #pragma unroll
       for (int r = 0; r < kFp8Reps; ++r) {
-        const int row = tid / 8 + r * (kThreads / 8), j = tid % 8;
+        const int row = stid / 8 + r * (kStreamThreads / 8), j = stid % 8;
         const int s0 = row * kRowBytes + (((2 * j) ^ swz_key(row)) << 4);
         const int s1 = row * kRowBytes + (((2 * j + 1) ^ swz_key(row)) << 4);
         *reinterpret_cast<bf16x8_t*>(kt_lds + s0) = fp8x8_to_bf16x8(k_stage[r][0], k_stage[r][1]);
@@ -413,13 +450,13 @@ __global__ __launch_bounds__(512) void prefill_kernel(
   const int plain_end = max(min((pos_first + 1) / kPage, kt_end), plain_begin);
   int buf = 0;
   auto advance = [&](int kt) {
-    if (kt + 1 < kt_end) {
+    if (kt + 1 < s_end) {
       if (buf == 0) issue_tile(kt + 1, std::integral_constant<int, 1>{});
       else issue_tile(kt + 1, std::integral_constant<int, 0>{});
     }
   };
   auto finish = [&](int kt) {
-    if (fp8 && kt + 1 < kt_end) {
+    if (fp8 && kt + 1 < s_end) {
       if (buf == 0) store_staged(std::integral_constant<int, 1>{});
       else store_staged(std::integral_constant<int, 0>{});
     }
@@ -437,45 +474,84 @@ __global__ __launch_bounds__(512) void prefill_kernel(
 
   // Only the sequence's last tile can hold slots past its end (whose V may be anything);
   // it runs last, on its own, with the V masking. Plain tiles lie wholly before the
-  // first new token, so the tail tile is never one of them.
+  // first new token, so the tail tile is never one of them. Each stream runs the three
+  // ranges clipped to its own tiles [s_begin, s_end).
   const bool tail_tile = kt_end * kPage > kv;
-  const int kt_stop = tail_tile ? kt_end - 1 : kt_end;
-  issue_tile(kt_begin, std::integral_constant<int, 0>{});
-  store_staged(std::integral_constant<int, 0>{});
+  const bool s_tail = tail_tile && s_end == kt_end;
+  const int s_stop = s_tail ? s_end - 1 : s_end;
+  const int p_begin = min(max(plain_begin, s_begin), s_end);
+  const int p_end = min(max(plain_end, p_begin), s_end);
+  if (s_end > s_begin) {
+    issue_tile(s_begin, std::integral_constant<int, 0>{});
+    store_staged(std::integral_constant<int, 0>{});
+  }
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-  for (int kt = kt_begin; kt < min(plain_begin, kt_stop); ++kt) masked_step(kt, std::false_type{});
+  for (int kt = s_begin; kt < min(p_begin, s_stop); ++kt) masked_step(kt, std::false_type{});
   {
     // the plain loop runs tile pairs on buffers (0, 1), so that every LDS buffer address
     // is an immediate; a first tile on buffer 1 and a last one on buffer 0 run alone
-    int kt = plain_begin;
-    if (kt < plain_end && buf == 1) {
+    int kt = p_begin;
+    if (kt < p_end && buf == 1) {
       advance(kt);
       compute(kt * kPage, buf, std::false_type{}, std::false_type{});
       finish(kt);
       ++kt;
     }
-    for (; kt + 1 < plain_end; kt += 2) {
-      if (kt + 1 < kt_end) issue_tile(kt + 1, std::integral_constant<int, 1>{});
+    for (; kt + 1 < p_end; kt += 2) {
+      if (kt + 1 < s_end) issue_tile(kt + 1, std::integral_constant<int, 1>{});
       compute(kt * kPage, std::integral_constant<int, 0>{}, std::false_type{}, std::false_type{});
-      if (fp8 && kt + 1 < kt_end) store_staged(std::integral_constant<int, 1>{});
+      if (fp8 && kt + 1 < s_end) store_staged(std::integral_constant<int, 1>{});
       __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();
-      if (kt + 2 < kt_end) issue_tile(kt + 2, std::integral_constant<int, 0>{});
+      if (kt + 2 < s_end) issue_tile(kt + 2, std::integral_constant<int, 0>{});
       compute((kt + 1) * kPage, std::integral_constant<int, 1>{}, std::false_type{}, std::false_type{});
-      if (fp8 && kt + 2 < kt_end) store_staged(std::integral_constant<int, 0>{});
+      if (fp8 && kt + 2 < s_end) store_staged(std::integral_constant<int, 0>{});
       __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();
     }
-    if (kt < plain_end) {
+    if (kt < p_end) {
       advance(kt);
       compute(kt * kPage, buf, std::false_type{}, std::false_type{});
       finish(kt);
       ++kt;
     }
   }
-  for (int kt = plain_end; kt < kt_stop; ++kt) masked_step(kt, std::false_type{});
-  if (tail_tile) masked_step(kt_end - 1, std::true_type{});
+  for (int kt = p_end; kt < s_stop; ++kt) masked_step(kt, std::false_type{});
+  if (s_tail) masked_step(s_end - 1, std::true_type{});
+
+  if constexpr (SPLIT) {
+    // Every wave has passed one barrier per tile of its stream plus the first; the
+    // first stream holds at most one tile fewer and passes the missing barrier here,
+    // so that both streams meet the barriers below together.
+    for (int i = s_end - s_begin; i < kt_end - kt_mid; ++i) __syncthreads();
+    __syncthreads();                   // every tile read is done: LDS is free
+    // the second stream's per-lane (max, sum, 64 accumulators), lane-contiguous, into
+    // 66 x 64 floats per row block (67.6 KB for 4 row blocks)
+    float* xch = reinterpret_cast<float*>(lds) + rwave * (66 * 64) + lane;
+    if (kstream == 1) {
+      xch[0] = m_run;
+      xch[64] = l_run;
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) xch[(2 + 16 * db + e) * 64] = acc[db][e];
+    }
+    __syncthreads();
+    if (kstream == 1) return;
+    // two partial softmaxes of one row over disjoint keys, each relative to its own
+    // running max (log2 units): rescale both to the larger; a stream that saw no key of
+    // the row (max -inf) contributes nothing
+    const float m_o = xch[0], l_o = xch[64];
+    const float m_new = fmaxf(m_run, m_o);
+    const float s_me = m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
+    const float s_o = m_o == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_o - m_new);
+    l_run = l_run * s_me + l_o * s_o;
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[db][e] = acc[db][e] * s_me + xch[(2 + 16 * db + e) * 64] * s_o;
+  }
 
   // ---- epilogue: 1/l, gate, bf16 store (lane owns row lr; d values
   // 32*db + 8*(v/4) + 4*half + (v%4))
@@ -507,22 +583,67 @@ __global__ __launch_bounds__(512) void prefill_kernel(
     }
 }
 
+// Launch bound: 512 threads, which also caps every shape at 256 VGPRs, i.e. 2 waves per
+// SIMD. One block per entry of the work list (PrefillGrid), plus idle padding blocks.
+template <int KIND, int KV>
+__global__ __launch_bounds__(512) void prefill_kernel(
+    LayerParams L, BatchParams B, CacheParams C, const uint16_t* __restrict__ q, int64_t q_stride,
+    const uint16_t* __restrict__ gate, int64_t gate_stride, const uint16_t* __restrict__ gate_bias,
+    uint16_t* out, int64_t out_stride, PrefillGrid P) {
+  constexpr bool kCanSplit = KIND == BEAM_LAYER_FULL;
+  __shared__ __attribute__((aligned(1024))) unsigned char lds[(kCanSplit ? 2 : 1) * 2 * 2 * kTileBytes];
+  const int lin = blockIdx.x;
+  const int xcd = lin % kNumXcds, slot = lin / kNumXcds;
+  int n, base, n_split;
+  prefill_xcd_plan(P, xcd, &n, &base, &n_split);
+  const int n_plain = n - n_split;
+  if (slot >= n_plain + 2 * n_split) return;             // padding
+  const bool split = slot >= n_plain;
+  const int j = slot - n_plain;                          // split blocks: 2 per unit
+  const int unit = split ? base + n_plain + j / 2 : base + slot;
+  const int tile = unit % P.tiles;
+  const int g = (unit / P.tiles) % L.Hkv;
+  const int b = unit / (P.tiles * L.Hkv);
+  constexpr int kRows = prefill_rows_per_block(KIND, false);
+  if constexpr (kCanSplit) {
+    if (split) {
+      prefill_rows<KIND, KV, true>(L, B, C, q, q_stride, gate, gate_stride, gate_bias, out, out_stride,
+                                   tile * kRows + (j % 2) * (kRows / 2), g, b, lds);
+      return;
+    }
+  }
+  prefill_rows<KIND, KV, false>(L, B, C, q, q_stride, gate, gate_stride, gate_bias, out, out_stride,
+                                tile * kRows, g, b, lds);
+}
+
 }  // namespace
 
 hipError_t launch_attn_prefill(const LayerParams& L, const BatchParams& B, const CacheParams& C,
-                               const void* q, int64_t q_stride, const void* gate,
-                               int64_t gate_stride, const void* gate_bias, void* out,
-                               int64_t out_stride, hipStream_t stream) {
+                               int split_mode, int cus, const void* q, int64_t q_stride,
+                               const void* gate, int64_t gate_stride, const void* gate_bias,
+                               void* out, int64_t out_stride, hipStream_t stream) {
   if (B.num_tokens == 0 || B.num_seqs == 0 || B.max_q_len == 0) return hipSuccess;
-  const int rows_per_block = prefill_waves(L.kind) * kRowsPerWave;
+  const int rows_per_block = prefill_rows_per_block(L.kind, false);
   const int64_t tiles = ((int64_t)B.max_q_len * L.G + rows_per_block - 1) / rows_per_block;
-  const dim3 grid((unsigned)tiles, (unsigned)L.Hkv, (unsigned)B.num_seqs),
-      block(prefill_waves(L.kind) * 64);
+  const int64_t units = tiles * L.Hkv * B.num_seqs;
+  if (units > 0x3FFFFFFF) return hipErrorInvalidValue;
+  PrefillGrid P;
+  P.units = (int32_t)units;
+  P.tiles = (int32_t)tiles;
+  P.split_mode = L.kind == BEAM_LAYER_FULL ? split_mode : 0;
+  P.cus_per_xcd = cus / kNumXcds > 0 ? cus / kNumXcds : 1;
+  int per_xcd = 0;
+  for (int x = 0; x < kNumXcds; ++x) {
+    int n, base, n_split;
+    prefill_xcd_plan(P, x, &n, &base, &n_split);
+    per_xcd = max(per_xcd, n + n_split);
+  }
+  const dim3 grid((unsigned)(per_xcd * kNumXcds)), block(prefill_waves(L.kind) * 64);
   auto launch = [&](auto kernel) {
     hipLaunchKernelGGL(kernel, grid, block, 0, stream, L, B, C, static_cast<const uint16_t*>(q),
                        q_stride, static_cast<const uint16_t*>(gate), gate_stride,
                        static_cast<const uint16_t*>(gate_bias), static_cast<uint16_t*>(out),
-                       out_stride);
+                       out_stride, P);
   };
   const bool f8 = C.dtype == BEAM_KV_FP8_E4M3;
   if (L.kind == BEAM_LAYER_SWA) {

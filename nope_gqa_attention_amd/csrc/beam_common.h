@@ -100,10 +100,21 @@ hipError_t launch_attn_decode(const LayerParams& L, const BatchParams& B, const 
                               const void* gate, int64_t gate_stride, const void* gate_bias,
                               void* out, int64_t out_stride, void* workspace, hipStream_t stream);
 
+// Prefill workgroups: 8 waves for full layers, 4 for sliding ones, one 32-row block per
+// wave; with the key split (full layers only) the 8 waves form two 4-wave streams over
+// the same 128 rows, each walking half of the key tiles.
+constexpr int prefill_waves(int kind) { return kind == BEAM_LAYER_SWA ? 4 : 8; }
+constexpr int prefill_rows_per_block(int kind, bool key_split) {
+  return 32 * (kind == BEAM_LAYER_SWA ? 4 : (key_split ? 4 : 8));
+}
+
+// split_mode: 0 no key split, 1 every row tile split, 2 the row tiles of a last round
+// that would leave at least half of an XCD idle (full layers; sliding ones never split);
+// cus: the device's compute units.
 hipError_t launch_attn_prefill(const LayerParams& L, const BatchParams& B, const CacheParams& C,
-                               const void* q, int64_t q_stride, const void* gate,
-                               int64_t gate_stride, const void* gate_bias, void* out,
-                               int64_t out_stride, hipStream_t stream);
+                               int split_mode, int cus, const void* q, int64_t q_stride,
+                               const void* gate, int64_t gate_stride, const void* gate_bias,
+                               void* out, int64_t out_stride, hipStream_t stream);
 
 // ---------------------------------------------------------------- device helpers
 
