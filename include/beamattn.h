@@ -167,7 +167,12 @@ beam_status beam_qknorm_rope_ssmax_kvwrite(const beam_layer_desc* layer, const b
  * tokens in its sequence produces nothing. Over an fp8 cache the codes are widened
  * exactly to bf16 on their way into the kernel's tiles; scores use sm_scale * k_scale
  * and the output is scaled by v_scale (chunked prefill with an fp8 KV cache, "SGLang
- * natively supports Reflection's Beam": the serving setup runs FP8 KV). */
+ * natively supports Reflection's Beam": the serving setup runs FP8 KV).
+ * On full layers with at least 1,024 keys the library may split a row tile's keys
+ * between two halves of its workgroup, which merge their partial softmaxes; results
+ * agree with the unsplit path within rounding. The environment variable
+ * BEAMATTN_PREFILL_KEY_SPLIT=0 turns this off and =1 splits every row tile (read on each
+ * call). Returns BEAM_ERR_INVALID_ARG when the launch would exceed 2^30 row tiles. */
 beam_status beam_attn_prefill(const beam_layer_desc* layer, const beam_batch* batch,
                               const beam_kv_cache* cache, const void* q, int64_t q_stride,
                               const void* gate, int64_t gate_stride, const void* gate_bias,

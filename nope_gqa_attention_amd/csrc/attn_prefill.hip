@@ -36,6 +36,11 @@
 //  * Tiles that every row of the workgroup sees whole run in a loop of their own with no
 //    mask; the masked tiles at the window start and at the diagonal run in separate
 //    loops, where tiles wholly outside a wave's rows skip compute.
+//  * One full-layer workgroup runs per CU at a time. When an XCD's share of row tiles
+//    would end in a round that leaves at least half of its CUs idle, each tile of that
+//    round runs as two workgroups of 128 rows whose waves form two streams over the two
+//    halves of the key tiles, merging their partial softmaxes in LDS (prefill_rows,
+//    SPLIT).
 #include <type_traits>
 #include <utility>
 
