@@ -501,10 +501,10 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(W == kDe
       if (gate != nullptr) {
         const u32x2_t gw = *reinterpret_cast<const u32x2_t*>(gate + tok * gate_stride + (int64_t)h * kHeadDim + d);
         const float bh = bf16_to_f32(gate_bias[h]);
-        y[0] *= 1.0f / (1.0f + expf(-(bf16_to_f32(gw[0] & 0xFFFFu) + bh)));
-        y[1] *= 1.0f / (1.0f + expf(-(bf16_to_f32(gw[0] >> 16) + bh)));
-        y[2] *= 1.0f / (1.0f + expf(-(bf16_to_f32(gw[1] & 0xFFFFu) + bh)));
-        y[3] *= 1.0f / (1.0f + expf(-(bf16_to_f32(gw[1] >> 16) + bh)));
+        y[0] *= gate_sigmoid(bf16_to_f32(gw[0] & 0xFFFFu) + bh);
+        y[1] *= gate_sigmoid(bf16_to_f32(gw[0] >> 16) + bh);
+        y[2] *= gate_sigmoid(bf16_to_f32(gw[1] & 0xFFFFu) + bh);
+        y[3] *= gate_sigmoid(bf16_to_f32(gw[1] >> 16) + bh);
       }
       const u32x2_t packed = {pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3])};
       *reinterpret_cast<u32x2_t*>(out + tok * out_stride + (int64_t)h * kHeadDim + d) = packed;
@@ -628,10 +628,10 @@ __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(
   const int d = 4 * q4;
   if (gate != nullptr) {
     const float bh = bf16_to_f32(gate_bias[h]);
-    y[0] *= 1.0f / (1.0f + expf(-(bf16_to_f32(gw[0] & 0xFFFFu) + bh)));
-    y[1] *= 1.0f / (1.0f + expf(-(bf16_to_f32(gw[0] >> 16) + bh)));
-    y[2] *= 1.0f / (1.0f + expf(-(bf16_to_f32(gw[1] & 0xFFFFu) + bh)));
-    y[3] *= 1.0f / (1.0f + expf(-(bf16_to_f32(gw[1] >> 16) + bh)));
+    y[0] *= gate_sigmoid(bf16_to_f32(gw[0] & 0xFFFFu) + bh);
+    y[1] *= gate_sigmoid(bf16_to_f32(gw[0] >> 16) + bh);
+    y[2] *= gate_sigmoid(bf16_to_f32(gw[1] & 0xFFFFu) + bh);
+    y[3] *= gate_sigmoid(bf16_to_f32(gw[1] >> 16) + bh);
   }
   const u32x2_t packed = {pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3])};
   *reinterpret_cast<u32x2_t*>(out + tok * out_stride + (int64_t)h * kHeadDim + d) = packed;

@@ -580,7 +580,7 @@ __device__ __forceinline__ void prefill_rows(
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const float gv = bf16_to_f32((gw[e / 2] >> (16 * (e % 2))) & 0xFFFFu) + bh;
-          y[e] *= 1.0f / (1.0f + expf(-gv));
+          y[e] *= gate_sigmoid(gv);
         }
       }
       const u32x2_t o = {pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3])};

@@ -185,6 +185,14 @@ __device__ __forceinline__ uint32_t e4m3_of_quotient(float x, float scale) {
   return f32_to_e4m3_sat(q, dir);
 }
 
+// Output gate sigmoid(x) = 1 / (1 + 2^(-x log2(e))) through the hardware exp2 and
+// reciprocal, each within about one binary32 ulp: a relative error of a few 1e-7, far
+// below the bf16 rounding of the gated output. x -> -inf: 2^+big = inf and 1/inf = 0, so
+// a closed gate gives exactly 0; x -> +inf: exactly 1.
+__device__ __forceinline__ float gate_sigmoid(float x) {
+  return __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(x * -1.4426950408889634f));
+}
+
 // Wave-wide helpers (wave64).
 // 8 OCP e4m3 codes (two little-endian words) -> 8 bf16 values; exact (every e4m3 value
 // is a bf16 value), scale 1.

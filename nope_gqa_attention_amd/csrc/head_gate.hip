@@ -35,9 +35,8 @@ __global__ __launch_bounds__(kThreads) void head_gate_kernel(
     for (int j = 0; j < 4; ++j) {
       const float a0 = bf16_to_f32(a[j] & 0xFFFFu), a1 = bf16_to_f32(a[j] >> 16);
       const float g0 = bf16_to_f32(g[j] & 0xFFFFu) + bh, g1 = bf16_to_f32(g[j] >> 16) + bh;
-      // sigmoid(x) = 1 / (1 + e^-x); e^-x = inf gives exactly 0
-      const float s0 = 1.0f / (1.0f + expf(-g0));
-      const float s1 = 1.0f / (1.0f + expf(-g1));
+      const float s0 = gate_sigmoid(g0);
+      const float s1 = gate_sigmoid(g1);
       o[j] = pack_bf16x2(a0 * s0, a1 * s1);
     }
     *reinterpret_cast<u32x4_t*>(out + t * out_stride + e) = o;
