@@ -24,8 +24,9 @@
 //  * P V uses O^T = V^T P^T: P^T is the score accumulator re-packed to bf16 in place;
 //    V^T comes from a row-major LDS copy of the V rows through the gfx950 transposing
 //    LDS read (ds_read_b64_tr_b16), so no register transpose is needed.
-//  * The running max is raised only when a row's maximum grows by more than 2^8 (log2
-//    domain), so the output rescale is skipped on almost every step.
+//  * Weights are formed against the running max first; the row max is only formed, and
+//    the running max raised, when some weight of a step exceeds 2^8 (or a row has no
+//    reference yet), so the max and the output rescale are skipped on almost every step.
 //  * The waves merge their (max, sum, output) in LDS; splits are merged by log-sum-exp
 //    in a second kernel, which also applies the gate; with one split the first kernel
 //    writes the gated output itself.
@@ -50,7 +51,7 @@ constexpr int merge_regions(int waves, int region_bytes) {
   return r;
 }
 constexpr float kLog2e = 1.4426950408889634f;
-constexpr float kRescaleSlack = 8.0f;                // log2 headroom before rescaling
+constexpr float kWeightCeiling = 256.0f;             // 2^8: a larger step sum raises the max
 constexpr int kBufferRsrcWord3 = 0x00020000;         // raw buffer, 32-bit data format (CDNA)
 constexpr int kLoadNonTemporal = 2;                  // cache-policy bit: nt
 
@@ -370,36 +371,40 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(W == kDe
             if (jk > row_pos[rb] || jk < row_lo[rb]) sv[4 * sb + v] = -INFINITY;
           }
       }
-      float mx = sv[0];
+      // Weights against the running max first, summed in bf16 pairs by v_dot2 (the
+      // values P V multiplies). Only when a lane's partial sum exceeds 2^8 (some weight
+      // grew past the slack, or overflowed) or a row has no reference yet does the wave
+      // form the row maximum, raise the running max and redo the weights.
+      bf16x8_t pb;
+      float part;
+      auto weights = [&](float mu) {
 #pragma unroll
-      for (int e = 1; e < 8; ++e) mx = fmaxf(mx, sv[e]);
-      mx = max_over_lane_groups(mx);
-      mx *= c;
-      // raise the running max only when some row's maximum grew by more than 2^8 (log2
-      // domain): the rescale of the output is then skipped on almost every step, and the
-      // final division by the running sum (accumulated against the same max) is exact
-      if (__builtin_amdgcn_ballot_w64(mx > m_run[rb] + kRescaleSlack) != 0) {
+        for (int e = 0; e < 8; ++e) pb[e] = (__bf16)__builtin_amdgcn_exp2f(fmaf(sv[e], c, -mu));
+        const bf16x2_t one = {(__bf16)1.0f, (__bf16)1.0f};
+        float ps = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; e += 2) {
+          const bf16x2_t pair = {pb[e], pb[e + 1]};
+          ps = __builtin_amdgcn_fdot2_f32_bf16(pair, one, ps, false);
+        }
+        part = ps;
+      };
+      weights(m_run[rb] == -INFINITY ? 0.f : m_run[rb]);
+      if (__builtin_amdgcn_ballot_w64(!(part <= kWeightCeiling) || (row_pos[rb] >= 0 && m_run[rb] == -INFINITY)) != 0) {
+        float mx = sv[0];
+#pragma unroll
+        for (int e = 1; e < 8; ++e) mx = fmaxf(mx, sv[e]);
+        mx = max_over_lane_groups(mx);
+        mx *= c;
         const float m_new = fmaxf(m_run[rb], mx);
         const float alpha = m_new == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m_run[rb] - m_new);
         l_run[rb] *= alpha;
 #pragma unroll
         for (int d = 0; d < 8; ++d) acc[rb][d] *= alpha;
         m_run[rb] = m_new;
+        weights(m_new == -INFINITY ? 0.f : m_new);
       }
-      const float m_use = m_run[rb] == -INFINITY ? 0.f : m_run[rb];
-      bf16x8_t pb;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) pb[e] = (__bf16)__builtin_amdgcn_exp2f(fmaf(sv[e], c, -m_use));
-      // the row sum adds the bf16-rounded weights that P V multiplies, two per
-      // instruction (v_dot2_f32_bf16 against ones, fp32 accumulation)
-      float ls = l_run[rb];
-#pragma unroll
-      for (int e = 0; e < 8; e += 2) {
-        const bf16x2_t pair = {pb[e], pb[e + 1]};
-        const bf16x2_t one = {(__bf16)1.0f, (__bf16)1.0f};
-        ls = __builtin_amdgcn_fdot2_f32_bf16(pair, one, ls, false);
-      }
-      l_run[rb] = ls;
+      l_run[rb] += part;
       pop[rb] = pb;
     }
     // ---- O^T += V^T P^T, V^T via transposing LDS reads

@@ -33,6 +33,7 @@ __global__ __launch_bounds__(kThreads) void qknorm_kvwrite_kernel(
     int64_t norm_w_head_stride, uint16_t* q_out, int64_t q_out_stride) {
   __shared__ float s_cos[kHeadDim / 2];
   __shared__ float s_sin[kHeadDim / 2];
+  __shared__ float s_qscale;
 
   const int64_t t = blockIdx.x;                 // token index in call order
   const int tid = threadIdx.x;
@@ -62,10 +63,12 @@ __global__ __launch_bounds__(kThreads) void qknorm_kvwrite_kernel(
     s_cos[tid] = (float)cd;
     s_sin[tid] = (float)sd;
   }
-  // SSMax scale (1 + p/base)^exponent, p = pos + 1, formed in fp64 and used in fp32
-  const float q_scale = swa ? 1.0f
-      : (float)pow(1.0 + (double)(pos + 1) / (double)L.ssmax_base, (double)L.ssmax_exponent);
+  // SSMax scale (1 + p/base)^exponent, p = pos + 1, formed once per token in fp64 and
+  // used in fp32
+  if (!swa && tid == 0)
+    s_qscale = (float)pow(1.0 + (double)(pos + 1) / (double)L.ssmax_base, (double)L.ssmax_exponent);
   __syncthreads();
+  const float q_scale = swa ? 1.0f : s_qscale;
 
   const int lane16 = tid % kLanesPerHead;       // which 8 values of the head
   const int head_slot = tid / kLanesPerHead;    // 0..15
