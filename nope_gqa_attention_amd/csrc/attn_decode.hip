@@ -17,10 +17,12 @@
 //    streams pages w, w+W, ... of its split: a 64-key page of one KV head is one
 //    contiguous 16 KiB (bf16) / 8 KiB (fp8) block, read in 32-key halves through
 //    non-temporal buffer loads.
-//  * Scores use MFMA 16x16x32 bf16 as S^T = K Q^T: K comes straight from global memory
-//    as the A operand (fp8 codes decoded to bf16 exactly in registers; the scale folds
-//    into the softmax scale), Q^T stays in registers. Each lane then owns one row's
-//    scores for 8 keys, so the online softmax needs only two cross-lane steps.
+//  * Scores use MFMA 16x16x32 bf16 as S^T = K Q^T: K rows are loaded whole and staged in
+//    LDS (bf16 rows, or fp8 codes as they are), then read in operand layout (fp8 codes
+//    decoded to bf16 exactly in registers; the scale folds into the softmax scale); Q^T
+//    stays in registers. The 12-wave kernel loads K straight into operand layout. Each
+//    lane then owns one row's scores for 8 keys, so the online softmax needs only two
+//    cross-lane steps.
 //  * P V uses O^T = V^T P^T: P^T is the score accumulator re-packed to bf16 in place;
 //    V^T comes from a row-major LDS copy of the V rows through the gfx950 transposing
 //    LDS read (ds_read_b64_tr_b16), so no register transpose is needed.
@@ -56,12 +58,15 @@ constexpr int kBufferRsrcWord3 = 0x00020000;         // raw buffer, 32-bit data 
 constexpr int kLoadNonTemporal = 2;                  // cache-policy bit: nt
 
 // Start of the 8-value slice of head dimension used by MFMA i (0..3) in lane group g
-// (lane / 16). K read from LDS (always bf16 there) or straight from a bf16 cache: one
-// 16-byte piece per MFMA; straight from an fp8 cache: one 16-byte load feeds 2 MFMAs.
+// (lane / 16). bf16 K (from LDS or straight from the cache): one 16-byte piece per MFMA;
+// fp8 K (raw codes, from LDS or straight from the cache): one 16-byte piece feeds 2 MFMAs.
 template <int KV, bool KST>
 __device__ __forceinline__ int dslice(int i, int g) {
-  return (KST || KV == BEAM_KV_BF16) ? 32 * i + 8 * g : 64 * (i / 2) + 16 * g + 8 * (i % 2);
+  return KV == BEAM_KV_BF16 ? 32 * i + 8 * g : 64 * (i / 2) + 16 * g + 8 * (i % 2);
 }
+// fp8 K staged in LDS as its raw codes: 128-byte rows padded to 144, so that the 16 rows
+// of one operand read (16 bytes each) fall in distinct bank groups
+constexpr int kK8RowBytes = kHeadDim + 16;
 
 
 // Max / sum over lanes l, l^16, l^32, l^48 (the four lane groups that hold one row's
@@ -307,7 +312,13 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(W == kDe
       // K and V rows of this half-step into LDS; the registers are then free for the
       // next half-step's loads, which fly during this step's compute. (Rows past the
       // sequence end: V is zeroed, K may hold anything -- those scores are masked.)
-      stage_rows(klds, kreg, kk0, false);
+      if constexpr (KV == BEAM_KV_BF16) {
+        stage_rows(klds, kreg, kk0, false);
+      } else {
+#pragma unroll
+        for (int it = 0; it < 4; ++it)
+          *reinterpret_cast<u32x4_t*>(klds + (lane / 8 + 8 * it) * kK8RowBytes + (lane % 8) * 16) = kreg[it];
+      }
       if (kk0 + 32 > kv) stage_rows(vlds, vreg, kk0, true);   // (the sequence's last keys)
       else stage_rows(vlds, vreg, kk0, false);
       if (kPipe && j + 1 < n_half) { fetch_k(j + 1); fetch_v(j + 1); }
@@ -317,13 +328,22 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(W == kDe
 #pragma unroll
     for (int sb = 0; sb < 2; ++sb) {
       bf16x8_t kop[4];
-      if (KST) {
+      if (KST && KV == BEAM_KV_BF16) {
         // MFMA layout from the staged rows: lane (lc, lg) reads row 16 sb + lc, dims
         // 32 i + 8 lg; the 16-byte row padding puts the 16 rows of one read in distinct
         // banks
 #pragma unroll
         for (int i = 0; i < 4; ++i)
           kop[i] = *reinterpret_cast<const bf16x8_t*>(klds + (16 * sb + lc) * kVRowBytes + (32 * i + 8 * lg) * 2);
+      } else if (KST) {
+        // raw fp8 rows: one 16-byte read of row 16 sb + lc (codes 64 jj + 16 lg ..) feeds
+        // MFMAs 2 jj and 2 jj + 1, widened exactly to bf16 here
+#pragma unroll
+        for (int jj = 0; jj < 2; ++jj) {
+          const u32x4_t w = *reinterpret_cast<const u32x4_t*>(klds + (16 * sb + lc) * kK8RowBytes + 64 * jj + 16 * lg);
+          kop[2 * jj] = fp8x8_to_bf16x8(w[0], w[1]);
+          kop[2 * jj + 1] = fp8x8_to_bf16x8(w[2], w[3]);
+        }
       } else if (KV == BEAM_KV_BF16) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) kop[i] = __builtin_bit_cast(bf16x8_t, kreg[4 * sb + i]);
