@@ -25,7 +25,8 @@
 //    cross-lane steps.
 //  * P V uses O^T = V^T P^T: P^T is the score accumulator re-packed to bf16 in place;
 //    V^T comes from a row-major LDS copy of the V rows through the gfx950 transposing
-//    LDS read (ds_read_b64_tr_b16), so no register transpose is needed.
+//    LDS reads (ds_read_b64_tr_b16 on bf16 rows; ds_read_b64_tr_b8 on raw fp8 rows,
+//    widened after the read), so no register transpose is needed.
 //  * Weights are formed against the running max first; the row max is only formed, and
 //    the running max raised, when some weight of a step exceeds 2^8 (or a row has no
 //    reference yet), so the max and the output rescale are skipped on almost every step.
@@ -38,6 +39,7 @@ namespace beam {
 namespace {
 
 constexpr int kVRowBytes = kHeadDim * 2 + 16;     // bf16 K or V row in LDS, padded
+                                                  // (fp8 rows use kK8RowBytes within it)
 constexpr int kVRowsPerWave = 32;                 // keys staged per half-page step
 // K goes through LDS as well in the 4-wave kernel (see fetch_k); the 12-wave kernel of
 // latency-bound launches keeps the V staging only, to fit its 12 waves in LDS.
@@ -67,6 +69,7 @@ __device__ __forceinline__ int dslice(int i, int g) {
 // fp8 K staged in LDS as its raw codes: 128-byte rows padded to 144, so that the 16 rows
 // of one operand read (16 bytes each) fall in distinct bank groups
 constexpr int kK8RowBytes = kHeadDim + 16;
+typedef int v2i32_t __attribute__((ext_vector_type(2)));
 
 
 // Max / sum over lanes l, l^16, l^32, l^48 (the four lane groups that hold one row's
@@ -294,14 +297,16 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(W == kDe
         *reinterpret_cast<u32x4_t*>(dst + r * kVRowBytes + lc * 16) = w;
       }
     } else {
+      // fp8 V rows as their raw codes, key r = 16 b + 4 g + e at LDS row 8 g + 4 b + e:
+      // the 8 keys one transposing read gathers (see the P V step) are then 8 consecutive
+      // rows, whose 144-byte pitch puts them in distinct banks
 #pragma unroll
       for (int it = 0; it < 4; ++it) {
         const int r = lane / 8 + 8 * it;
-        const int cc = lane % 8;
+        const int row = 8 * ((r % 16) / 4) + 4 * (r / 16) + r % 4;
         u32x4_t w = reg[it];
         if (zero_tail && kk0 + r >= kv) w = u32x4_t{0u, 0u, 0u, 0u};
-        *reinterpret_cast<bf16x8_t*>(dst + r * kVRowBytes + cc * 32) = fp8x8_to_bf16x8(w[0], w[1]);
-        *reinterpret_cast<bf16x8_t*>(dst + r * kVRowBytes + cc * 32 + 16) = fp8x8_to_bf16x8(w[2], w[3]);
+        *reinterpret_cast<u32x4_t*>(dst + row * kK8RowBytes + (lane % 8) * 16) = w;
       }
     }
   };
@@ -430,16 +435,27 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(W == kDe
     // ---- O^T += V^T P^T, V^T via transposing LDS reads
 #pragma unroll
     for (int db = 0; db < 8; ++db) {
-      const int col = 16 * db + 4 * (lc % 4);
-      const unsigned char* a0 = vlds + (4 * lg + lc / 4) * kVRowBytes + col * 2;
-      const unsigned char* a1 = vlds + (16 + 4 * lg + lc / 4) * kVRowBytes + col * 2;
-      const i16x4_t t0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (__attribute__((address_space(3))) i16x4_t*)(a0));
-      const i16x4_t t1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (__attribute__((address_space(3))) i16x4_t*)(a1));
-      const u32x2_t u0 = __builtin_bit_cast(u32x2_t, t0), u1 = __builtin_bit_cast(u32x2_t, t1);
-      const u32x4_t uv = {u0[0], u0[1], u1[0], u1[1]};
-      const bf16x8_t vop = __builtin_bit_cast(bf16x8_t, uv);
+      bf16x8_t vop;
+      if constexpr (KV == BEAM_KV_BF16) {
+        const int col = 16 * db + 4 * (lc % 4);
+        const unsigned char* a0 = vlds + (4 * lg + lc / 4) * kVRowBytes + col * 2;
+        const unsigned char* a1 = vlds + (16 + 4 * lg + lc / 4) * kVRowBytes + col * 2;
+        const i16x4_t t0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) i16x4_t*)(a0));
+        const i16x4_t t1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) i16x4_t*)(a1));
+        const u32x2_t u0 = __builtin_bit_cast(u32x2_t, t0), u1 = __builtin_bit_cast(u32x2_t, t1);
+        const u32x4_t uv = {u0[0], u0[1], u1[0], u1[1]};
+        vop = __builtin_bit_cast(bf16x8_t, uv);
+      } else {
+        // ds_read_b64_tr_b8: in each 16-lane group, lane i receives byte i % 8 of the
+        // 8-byte pieces addressed by lanes 2 j + i / 8, j = 0..7. Lane 2 j + h addresses
+        // LDS row 8 lg + j (key slot j of this lane group) at codes 16 db + 8 h, so lane
+        // lc gets dimension 16 db + lc of its 8 keys, in the k-slot order of P^T
+        const unsigned char* a = vlds + (8 * lg + (lc >> 1)) * kK8RowBytes + 16 * db + 8 * (lc & 1);
+        const v2i32_t t = __builtin_amdgcn_ds_read_tr8_b64_v2i32((__attribute__((address_space(3))) v2i32_t*)(a));
+        vop = fp8x8_to_bf16x8((uint32_t)t[0], (uint32_t)t[1]);
+      }
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb)
         acc[rb][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, pop[rb], acc[rb][db], 0, 0, 0);
