@@ -242,9 +242,10 @@ beam_status beam_head_gate(const beam_layer_desc* layer, int64_t num_tokens,
  * fused norm kernel, whose strided inputs are column ranges of its output) and o_proj
  * (6144 -> 5120). y[i][j] = bf16(sum_c x[i][c] * w[j][c]) with fp32 accumulation.
  *  m, n, k  rows of x (tokens), output features, input features; k % 64 == 0, n % 4 == 0
- *  x        device bf16 [m][k], row stride x_stride (>= k, a multiple of 8)
+ *  x        device bf16 [m][k], row stride x_stride (>= k, a multiple of 8, at most
+ *           4,194,303)
  *  w        device bf16 [n][k] (the weight in its [out][in] layout), row stride w_stride
- *           (>= k, a multiple of 8)
+ *           (>= k, a multiple of 8, at most 4,194,303)
  *  y        device bf16 [m][n], row stride y_stride (>= n, a multiple of 8); must not
  *           overlap x or w
  * m == 0 launches nothing. Sized for prefill token counts (tiles of 256 tokens x 256

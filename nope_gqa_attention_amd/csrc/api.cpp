@@ -532,6 +532,10 @@ beam_status beam_linear_bf16(int64_t m, int64_t n, int64_t k, const void* x, int
   beam_status s;
   if ((s = check_tensor("x", x, x_stride, k, m)) != BEAM_OK) return s;
   if ((s = check_tensor("w", w, w_stride, k, n)) != BEAM_OK) return s;
+  // the kernel reads a 256-row tile of x or w through 32-bit byte offsets
+  if (x_stride > (int64_t)0x7FFFFFFF / 512 || w_stride > (int64_t)0x7FFFFFFF / 512)
+    return fail(BEAM_ERR_INVALID_ARG, "linear x and w row strides must be at most %lld elements",
+                (long long)((int64_t)0x7FFFFFFF / 512));
   if ((s = check_tensor("y", y, y_stride, n, m)) != BEAM_OK) return s;
   if (m > 0) {
     const int64_t xb = ((m - 1) * x_stride + k) * 2, wb = ((n - 1) * w_stride + k) * 2,

@@ -84,6 +84,20 @@ int main(void) {
                            NULL) == BEAM_OK);
   }
 
+  /* the projection GEMM: k must be a multiple of 64, and a 256-row tile of x or w must
+   * span fewer than 2^31 bytes (row strides up to 4,194,303 elements); the checks fail
+   * before any launch, so host pointers stand in for device buffers */
+  {
+    static uint64_t fake[64];
+    CHECK(beam_linear_bf16(16, 64, 100, fake, 128, fake, 128, fake + 32, 64, NULL) ==
+          BEAM_ERR_INVALID_ARG);
+    CHECK(beam_linear_bf16(16, 64, 64, fake, 4194304, fake, 64, fake + 32, 64, NULL) ==
+          BEAM_ERR_INVALID_ARG);
+    CHECK(strstr(beam_last_error(), "stride") != NULL);
+    CHECK(beam_linear_bf16(16, 64, 64, fake, 64, fake, 4194304, fake + 32, 64, NULL) ==
+          BEAM_ERR_INVALID_ARG);
+  }
+
   if (!failures) printf("ok\n");
   return failures;
 }
