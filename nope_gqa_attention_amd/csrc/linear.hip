@@ -112,20 +112,28 @@ __global__ __launch_bounds__(kLinThreads) void linear_bf16_kernel(
   auto compute = [&](int buf) {
     const unsigned char* wt = lds + buf * 2 * kLinTileBytes + (64 * wn) * kLinRowBytes;
     const unsigned char* xt = lds + buf * 2 * kLinTileBytes + kLinTileBytes + (128 * wm) * kLinRowBytes;
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-      bf16x8_t a[2], bop[4];
+    // operands of k step kk + 1 are read (second register set) while step kk's MFMAs run;
+    // the scheduling barriers keep the two sets apart
+    bf16x8_t a[2][2], bop[2][4];
+    auto load = [&](int kk, int set) {
 #pragma unroll
       for (int nb = 0; nb < 2; ++nb)
-        a[nb] = *reinterpret_cast<const bf16x8_t*>(wt + nb * 32 * kLinRowBytes + op_off[kk]);
+        a[set][nb] = *reinterpret_cast<const bf16x8_t*>(wt + nb * 32 * kLinRowBytes + op_off[kk]);
 #pragma unroll
       for (int mb = 0; mb < 4; ++mb)
-        bop[mb] = *reinterpret_cast<const bf16x8_t*>(xt + mb * 32 * kLinRowBytes + op_off[kk]);
+        bop[set][mb] = *reinterpret_cast<const bf16x8_t*>(xt + mb * 32 * kLinRowBytes + op_off[kk]);
+    };
+    load(0, 0);
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      if (kk + 1 < 4) load(kk + 1, (kk + 1) & 1);
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int nb = 0; nb < 2; ++nb)
 #pragma unroll
         for (int mb = 0; mb < 4; ++mb)
-          acc[nb][mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[nb], bop[mb], acc[nb][mb], 0, 0, 0);
+          acc[nb][mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[kk & 1][nb], bop[kk & 1][mb], acc[nb][mb], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
     }
   };
 
