@@ -38,10 +38,13 @@ Readings taken where the pages are silent (each is listed in the design notes):
     code is the nearest e4m3 value to the exact quotient.
 
 Parity status: every function below is pinned by the CPU test-suite against closed
-forms, library routines or invariants, except the readings above that no page fixes
-(RoPE pairing, norm-weight shape, window +-1, GQA head mapping, fp8 scale choice):
-for those the oracle is "parity unpinned" against the pages and pinned only to the
-stated reading.
+forms, library routines or invariants. The readings above that no page fixes are pinned
+to the open implementations of the same components in the `transformers` library:
+the window and causal masks (masking_utils), the query-head -> KV-head mapping
+(Llama's repeat_kv), the rotary pairing, direction and frequencies (Llama's rotary
+embedding) and the per-head norm with one [head_dim] weight (Qwen3's q_norm). The fp8
+scale choice (per tensor, amax/448) is a property of the generated inputs; the oracle
+takes the scale as given ("parity unpinned" for that choice only).
 """
 
 from __future__ import annotations

@@ -5,6 +5,7 @@ import numpy as np
 import pytest
 
 import oracle.beam_oracle as B
+import tests.test_oracle_conventions as conv
 import tests.test_oracle_pins as pins
 
 
@@ -115,6 +116,29 @@ def _bf16_round_via_binary32(x):
     return _ORIG_BF16_ROUND(np.asarray(x, dtype=np.float64).astype(np.float32).astype(np.float64))
 
 
+def _rope_interleaved_pairs(y, pos, theta=B.ROPE_THETA):
+    # pairs (2i, 2i + 1) instead of (i, i + D/2)
+    y = np.asarray(y, dtype=np.float64)
+    ang = np.asarray(pos, dtype=np.float64)[..., None] * B.rope_inv_freq(y.shape[-1], theta)
+    c, s = np.cos(ang), np.sin(ang)
+    a, b = y[..., 0::2], y[..., 1::2]
+    out = np.empty_like(y)
+    out[..., 0::2] = a * c - b * s
+    out[..., 1::2] = b * c + a * s
+    return out
+
+
+def _inv_freq_over_half_dim(head_dim=B.HEAD_DIM, theta=B.ROPE_THETA):
+    i = np.arange(head_dim // 2, dtype=np.float64)
+    return np.power(theta, -i / head_dim)
+
+
+def _rms_over_all_heads(x, w, eps=B.RMS_EPS):
+    x = np.asarray(x, dtype=np.float64)
+    ms = np.mean(x * x, axis=(-2, -1), keepdims=True)
+    return np.asarray(w, dtype=np.float64) * x / np.sqrt(ms + eps)
+
+
 MUTATIONS = [
     ("store_kv", _store_binary32_quotient, pins.test_fp8_store_is_nearest_e4m3_of_exact_quotient),
     ("prepare_qk", lambda *a, **k: _prepare(*a, order="rotate-first"),
@@ -132,6 +156,12 @@ MUTATIONS = [
     ("f64_to_e4m3", _e4m3_ties_away, pins.test_e4m3_encode_all_bf16_inputs_match_torch_after_clamp),
     ("bf16_round", _bf16_truncate, pins.test_bf16_round_matches_torch_cast),
     ("SM_SCALE", 1.0 / 128.0, pins.test_attention_matches_sdpa_textbook_routine),
+    ("visible_range", _window_off_by_one, conv.test_sliding_window_and_causal_visibility_match_transformers_masks),
+    ("attend", _attend_wrong_group, conv.test_query_heads_read_kv_heads_as_repeat_kv_maps_them),
+    ("rope", _rope_wrong_sign, conv.test_rope_rotation_matches_llama_apply_rotary_pos_emb),
+    ("rope", _rope_interleaved_pairs, conv.test_rope_rotation_matches_llama_apply_rotary_pos_emb),
+    ("rope_inv_freq", _inv_freq_over_half_dim, conv.test_rope_frequencies_match_llama_rotary_embedding),
+    ("rms_norm", _rms_over_all_heads, conv.test_per_head_rms_norm_with_one_weight_matches_qwen3_q_norm),
 ]
 
 
