@@ -5,8 +5,12 @@ import numpy as np
 import pytest
 
 import oracle.beam_oracle as B
-import tests.test_oracle_conventions as conv
 import tests.test_oracle_pins as pins
+
+try:  # the convention pins need the transformers library; the other pins do not
+    import tests.test_oracle_conventions as conv
+except pytest.skip.Exception:
+    conv = None
 
 
 def _window_off_by_one(pos, kind, window=B.WINDOW):
@@ -156,13 +160,16 @@ MUTATIONS = [
     ("f64_to_e4m3", _e4m3_ties_away, pins.test_e4m3_encode_all_bf16_inputs_match_torch_after_clamp),
     ("bf16_round", _bf16_truncate, pins.test_bf16_round_matches_torch_cast),
     ("SM_SCALE", 1.0 / 128.0, pins.test_attention_matches_sdpa_textbook_routine),
-    ("visible_range", _window_off_by_one, conv.test_sliding_window_and_causal_visibility_match_transformers_masks),
-    ("attend", _attend_wrong_group, conv.test_query_heads_read_kv_heads_as_repeat_kv_maps_them),
-    ("rope", _rope_wrong_sign, conv.test_rope_rotation_matches_llama_apply_rotary_pos_emb),
-    ("rope", _rope_interleaved_pairs, conv.test_rope_rotation_matches_llama_apply_rotary_pos_emb),
-    ("rope_inv_freq", _inv_freq_over_half_dim, conv.test_rope_frequencies_match_llama_rotary_embedding),
-    ("rms_norm", _rms_over_all_heads, conv.test_per_head_rms_norm_with_one_weight_matches_qwen3_q_norm),
 ]
+if conv is not None:
+    MUTATIONS += [
+        ("visible_range", _window_off_by_one, conv.test_sliding_window_and_causal_visibility_match_transformers_masks),
+        ("attend", _attend_wrong_group, conv.test_query_heads_read_kv_heads_as_repeat_kv_maps_them),
+        ("rope", _rope_wrong_sign, conv.test_rope_rotation_matches_llama_apply_rotary_pos_emb),
+        ("rope", _rope_interleaved_pairs, conv.test_rope_rotation_matches_llama_apply_rotary_pos_emb),
+        ("rope_inv_freq", _inv_freq_over_half_dim, conv.test_rope_frequencies_match_llama_rotary_embedding),
+        ("rms_norm", _rms_over_all_heads, conv.test_per_head_rms_norm_with_one_weight_matches_qwen3_q_norm),
+    ]
 
 
 @pytest.mark.parametrize("name,bad,pin", MUTATIONS, ids=[f"{m[0]}-{i}" for i, m in enumerate(MUTATIONS)])
