@@ -140,12 +140,23 @@ __global__ __launch_bounds__(kLinThreads) void linear_bf16_kernel(
   issue_stage(0, 0);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-  for (int64_t ks = 0; ks < nk; ++ks) {
-    const int buf = (int)(ks & 1);
-    if (ks + 1 < nk) issue_stage(ks + 1, buf ^ 1);
-    compute(buf);
+  // stages in pairs on buffers (0, 1), so that every LDS operand address is a lane
+  // constant plus an immediate
+  int64_t ks = 0;
+  for (; ks + 1 < nk; ks += 2) {
+    issue_stage(ks + 1, 1);
+    compute(0);
     __builtin_amdgcn_s_waitcnt(0);     // this wave's copies of the next stage landed
     __syncthreads();                   // ... and everyone's; this buffer is free again
+    if (ks + 2 < nk) issue_stage(ks + 2, 0);
+    compute(1);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+  }
+  if (ks < nk) {                       // an odd last stage, on buffer 0
+    compute(0);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
   }
 
   // ---- epilogue: lane holds D[n][m] for m = its column, n = 4 consecutive values per
