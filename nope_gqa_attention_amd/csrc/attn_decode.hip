@@ -275,13 +275,12 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(W == kDe
     for (int i = 0; i < kVRegs; ++i) vreg[i] = __builtin_amdgcn_raw_buffer_load_b128(r, voff[i], 0, kLoadNonTemporal);
   };
   // With 2 waves per SIMD the loop is software-pipelined inside the one register set: the
-  // next half-step's K loads are issued as soon as the score MFMAs have read this step's
-  // K, and its V loads once V is staged in LDS, so they fly during the softmax and P V
-  // (-11% time on the 8-token 1M-key verify, -7% on batch-1 bf16 decode against the
-  // unpipelined loop at 3 waves per SIMD). One block over an fp8 cache keeps 3 resident
-  // waves and the plain loop (faster there: each half-step is half the bytes); bf16 with
-  // three blocks has no registers to spare; the wide single-split workgroups run at 3
-  // waves per SIMD.
+  // next half-step's K and V loads are issued once this step's K and V are staged in LDS,
+  // so they fly during this step's scores, softmax and P V (-11% time on the 8-token
+  // 1M-key verify, -7% on batch-1 bf16 decode against the unpipelined loop at 3 waves per
+  // SIMD). bf16 with three blocks has no registers to spare and fetches, then computes;
+  // so do the wide single-split workgroups (3 waves per SIMD, K loaded straight into
+  // operand layout).
   constexpr bool kPipe = W == kDecodeWaves && decode_wgs_per_cu(RB, KV) == 2 &&
                          !(KV == BEAM_KV_BF16 && RB == 3);
 
