@@ -22,7 +22,9 @@
 //  * Full layers: 8 waves (2 per SIMD) x 32 rows = 256 rows per workgroup. Sliding
 //    layers: 4 waves x 32 rows, two workgroups per CU, so that one workgroup's start-up
 //    (Q rows, first tile) and end (output) overlap the other's compute -- a sliding row
-//    tile only spans about 9 key tiles. Per 32-key half of a tile a wave computes
+//    tile only spans about 9 key tiles. Their rows of q, gate and out also pass through
+//    LDS, so that every global access moves whole rows (see prefill_rows). Per 32-key
+//    half of a tile a wave computes
 //    S^T = K Q^T with MFMA 32x32x16 bf16 (K from LDS, Q^T held in registers); a lane
 //    then holds 16 scores of one row, so row max/sum take one cross-half swap
 //    (permlane32).
@@ -72,6 +74,9 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const char* base, in
 __device__ __forceinline__ void copy16_to_lds(__amdgpu_buffer_rsrc_t r, uint32_t off, lds_void_t* dst) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, dst, 16, off, 0, 0, 0);
 }
+// Lane offsets of a row-data buffer resource (rows of q, gate or out) that lie past its
+// range: loads through them return zero and stores are dropped.
+constexpr uint32_t kRowRange = 0x80000000u;
 
 // Chunk slot of 16-byte chunk c (0..15) of row r in a swizzled tile: c XOR f(r mod 16),
 // f swapping the two 2-bit halves of r's low nibble. f is a bijection, so the 16 rows a
@@ -220,7 +225,43 @@ __device__ __forceinline__ void prefill_rows(
   const bool row_valid = wave_active && lr < wrows;
   const int row_pos = row_valid ? first_pos + my_row / L.G : -1;
   const int row_lo = (swa && row_valid) ? max(row_pos - L.window + 1, 0) : 0;
-  {
+
+  // Sliding layers: a row tile sees only about nine key tiles, so moving its rows of q,
+  // gate and out is a large share of its time. These go through LDS, so that each global
+  // access instruction moves whole 256-byte rows (4 rows, 1 KiB): Q is copied straight
+  // into the second tile buffer with the first tile, the gate into the free buffer during
+  // the last tile, and the gated output is assembled in place of the gate, then stored
+  // row by row. Each wave moves its own 32 rows, swizzled like the K/V tiles. Row R of
+  // the tile is token t_first + (r0m + R) / G, head g G + (r0m + R) % G.
+  constexpr bool kRowLds = swa && !SPLIT;
+  const int t_first = tile_row0 / L.G;
+  const int r0m = tile_row0 - t_first * L.G;
+  const float inv_g = 1.0f / (float)L.G;
+  // byte offset of chunk slot (lane % 16) of row 32 rwave + 4 i + lane / 16 in a row
+  // tensor of token stride `stride` (elements), relative to token t_first; past the
+  // tile's rows, an offset outside the buffer range
+  auto row_off = [&](int i, int64_t stride, int ln) -> uint32_t {
+    const int r = 32 * rwave + 4 * i + ln / 16;
+    const int x = r0m + r;
+    const int t = (int)(((float)x + 0.5f) * inv_g);
+    const int hh = x - t * L.G;
+    const int chunk = (ln % 16) ^ swz_key(r);
+    const uint32_t off = (uint32_t)(t * (int)stride + (g * L.G + hh) * kHeadDim) * 2u + chunk * 16;
+    return r < tile_rows ? off : kRowRange;
+  };
+  auto row_rsrc = [&](const uint16_t* base, int64_t stride) {
+    return tile_rsrc(reinterpret_cast<const char*>(base + (int64_t)(q0 + t_first) * stride), (int)kRowRange);
+  };
+  // copy this wave's 32 rows of a row tensor into LDS at `dst` (+ 32 rwave rows)
+  auto issue_rows = [&](const uint16_t* base, int64_t stride, int dst) {
+    const __amdgpu_buffer_rsrc_t r = row_rsrc(base, stride);
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      copy16_to_lds(r, row_off(i, stride, ln), (lds_void_t*)(lds + dst + (32 * rwave + 4 * i) * kRowBytes));
+  };
+  if constexpr (!kRowLds) {
     const int t = row_valid ? my_row / L.G : 0;
     const int h = g * L.G + (row_valid ? my_row % L.G : 0);
     const uint16_t* qrow = q + (int64_t)(q0 + t) * q_stride + (int64_t)h * kHeadDim;
@@ -454,10 +495,21 @@ __device__ __forceinline__ void prefill_rows(
   const int plain_begin = min(max((blk_max_lo + kPage - 1) / kPage, kt_begin), kt_end);
   const int plain_end = max(min((pos_first + 1) / kPage, kt_end), plain_begin);
   int buf = 0;
+  int gate_buf = 0;        // (kRowLds) the LDS buffer the gate rows were copied into
+  auto issue_gate = [&](int to_buf) {
+    if constexpr (kRowLds) {
+      if (gate != nullptr) {
+        gate_buf = to_buf;
+        issue_rows(gate, gate_stride, to_buf * 2 * kTileBytes);
+      }
+    }
+  };
   auto advance = [&](int kt) {
     if (kt + 1 < s_end) {
       if (buf == 0) issue_tile(kt + 1, std::integral_constant<int, 1>{});
       else issue_tile(kt + 1, std::integral_constant<int, 0>{});
+    } else {
+      issue_gate(buf ^ 1);     // the last tile: the gate rows go into the free buffer
     }
   };
   auto finish = [&](int kt) {
@@ -490,8 +542,18 @@ __device__ __forceinline__ void prefill_rows(
     issue_tile(s_begin, std::integral_constant<int, 0>{});
     store_staged(std::integral_constant<int, 0>{});
   }
+  if constexpr (kRowLds) issue_rows(q, q_stride, 2 * kTileBytes);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
+  if constexpr (kRowLds) {
+    // this lane's row of Q from buffer 1, then every wave is done with it before the
+    // second tile is copied there
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      qop[i] = *reinterpret_cast<const bf16x8_t*>(lds + 2 * kTileBytes + (32 * rwave + lr) * kRowBytes +
+                                                  (((2 * i + half) ^ swz_key(lr)) << 4));
+    __syncthreads();
+  }
   for (int kt = s_begin; kt < min(p_begin, s_stop); ++kt) masked_step(kt, std::false_type{});
   {
     // the plain loop runs tile pairs on buffers (0, 1), so that every LDS buffer address
@@ -510,6 +572,7 @@ __device__ __forceinline__ void prefill_rows(
       __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();
       if (kt + 2 < s_end) issue_tile(kt + 2, std::integral_constant<int, 0>{});
+      else issue_gate(0);
       compute((kt + 1) * kPage, std::integral_constant<int, 1>{}, std::false_type{}, std::false_type{});
       if (fp8 && kt + 2 < s_end) store_staged(std::integral_constant<int, 0>{});
       __builtin_amdgcn_s_waitcnt(0);
@@ -561,6 +624,45 @@ __device__ __forceinline__ void prefill_rows(
   // ---- epilogue: 1/l, gate, bf16 store (lane owns row lr; d values
   // 32*db + 8*(v/4) + 4*half + (v%4))
   const float lsum = swap_halves_sum(l_run);
+  if constexpr (kRowLds) {
+    if (!wave_active) return;
+    // every tile is done (the last tile's barrier), so both buffers are free; this
+    // wave's rows: the gate's, or buffer 0 without a gate
+    const int rows_at = (gate != nullptr ? gate_buf * 2 * kTileBytes : 0) + 32 * rwave * kRowBytes;
+    if (row_valid) {
+      const float inv = lsum > 0.f ? (fp8 ? C.v_scale : 1.0f) / lsum : 0.f;
+      const int h = g * L.G + my_row % L.G;
+      const float bh = gate != nullptr ? bf16_to_f32(gate_bias[h]) : 0.f;
+      unsigned char* rl = lds + rows_at + lr * kRowBytes + 8 * half;
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          // d = 32 db + 8 q4 + 4 half + e: bytes 8 half.. of chunk 4 db + q4
+          u32x2_t* pr = reinterpret_cast<u32x2_t*>(rl + (((4 * db + q4) ^ swz_key(lr)) << 4));
+          float y[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) y[e] = acc[db][4 * q4 + e] * inv;
+          if (gate != nullptr) {
+            const u32x2_t gw = *pr;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const float gv = bf16_to_f32((gw[e / 2] >> (16 * (e % 2))) & 0xFFFFu) + bh;
+              y[e] *= gate_sigmoid(gv);
+            }
+          }
+          *pr = u32x2_t{pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3])};
+        }
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");    // the wave's output rows are in LDS
+    const __amdgpu_buffer_rsrc_t ro = row_rsrc(out, out_stride);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const u32x4_t v = *reinterpret_cast<const u32x4_t*>(lds + rows_at + (4 * i + lane / 16) * kRowBytes + (lane % 16) * 16);
+      __builtin_amdgcn_raw_buffer_store_b128(v, ro, row_off(i, out_stride, lane), 0, 0);
+    }
+    return;
+  }
   if (!row_valid) return;
   const int t = my_row / L.G;
   const int h = g * L.G + my_row % L.G;

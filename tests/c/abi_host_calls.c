@@ -98,6 +98,36 @@ int main(void) {
           BEAM_ERR_INVALID_ARG);
   }
 
+  /* sliding-layer prefill moves a row tile's q, gate and out rows through 32-bit
+   * offsets: token strides above 4,194,303 elements are refused before any launch */
+  {
+    static uint64_t fake[64];
+    static int32_t meta[4];
+    beam_kv_cache cache;
+    beam_batch one;
+    memset(&cache, 0, sizeof cache);
+    memset(&one, 0, sizeof one);
+    cache.k = fake;
+    cache.v = fake + 32;
+    cache.num_pages = 1;
+    cache.dtype = BEAM_KV_BF16;
+    one.num_seqs = 1;
+    one.q_start = meta;
+    one.kv_len = meta + 2;
+    one.block_table = meta + 3;
+    one.max_pages = 1;
+    one.max_q_len = 1;
+    one.max_kv_len = 1;
+    one.num_tokens = 1;
+    CHECK(beam_attn_prefill(&swa, &one, &cache, fake, 4194304, NULL, 0, NULL, fake + 32, 6144,
+                            NULL) == BEAM_ERR_INVALID_ARG);
+    CHECK(strstr(beam_last_error(), "stride") != NULL);
+    CHECK(beam_attn_prefill(&swa, &one, &cache, fake, 6144, fake, 4194304, fake, fake + 32, 6144,
+                            NULL) == BEAM_ERR_INVALID_ARG);
+    CHECK(beam_attn_prefill(&swa, &one, &cache, fake, 6144, NULL, 0, NULL, fake + 32, 4194304,
+                            NULL) == BEAM_ERR_INVALID_ARG);
+  }
+
   if (!failures) printf("ok\n");
   return failures;
 }
