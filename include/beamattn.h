@@ -172,9 +172,8 @@ beam_status beam_qknorm_rope_ssmax_kvwrite(const beam_layer_desc* layer, const b
  * between two halves of its workgroup, which merge their partial softmaxes; results
  * agree with the unsplit path within rounding. The environment variable
  * BEAMATTN_PREFILL_KEY_SPLIT=0 turns this off and =1 splits every row tile (read on each
- * call). Returns BEAM_ERR_INVALID_ARG when the launch would exceed 2^30 row tiles, or,
- * for sliding layers, when q_stride, out_stride or (gated) gate_stride exceeds 4,194,303
- * elements. */
+ * call). Returns BEAM_ERR_INVALID_ARG when the launch would exceed 2^30 row tiles, or
+ * when q_stride, out_stride or (gated) gate_stride exceeds 4,194,303 elements. */
 beam_status beam_attn_prefill(const beam_layer_desc* layer, const beam_batch* batch,
                               const beam_kv_cache* cache, const void* q, int64_t q_stride,
                               const void* gate, int64_t gate_stride, const void* gate_bias,

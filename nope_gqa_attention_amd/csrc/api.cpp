@@ -233,7 +233,7 @@ beam_status check_cache(const beam_kv_cache* C, beam::CacheParams* out) {
   return BEAM_OK;
 }
 
-// Largest token stride (elements) of q, gate and out for sliding-layer prefill.
+// Largest token stride (elements) of q, gate and out for prefill.
 constexpr int64_t kMaxRowStride = 4194303;
 
 beam_status check_tensor(const char* name, const void* p, int64_t stride, int64_t min_stride,
@@ -395,11 +395,10 @@ beam_status beam_attn_prefill(const beam_layer_desc* layer, const beam_batch* ba
   if ((s = check_gate(gate, gate_stride, gate_bias, L.Hq, N)) != BEAM_OK) return s;
   if ((int64_t)B.max_q_len * L.G > 0x7FFFFFFF)
     return fail(BEAM_ERR_INVALID_ARG, "max_q_len * query heads per KV head must fit in int32");
-  // sliding layers move a row tile's q, gate and out rows through 32-bit offsets from
-  // the tile's first token (at most 128 tokens on)
-  if (L.kind == BEAM_LAYER_SWA &&
-      (q_stride > kMaxRowStride || out_stride > kMaxRowStride || (gate != nullptr && gate_stride > kMaxRowStride)))
-    return fail(BEAM_ERR_INVALID_ARG, "sliding-layer prefill token strides must be at most %lld elements",
+  // a row tile's q, gate and out rows move through 32-bit offsets from the tile's first
+  // token (at most 255 tokens on)
+  if (q_stride > kMaxRowStride || out_stride > kMaxRowStride || (gate != nullptr && gate_stride > kMaxRowStride))
+    return fail(BEAM_ERR_INVALID_ARG, "prefill token strides must be at most %lld elements",
                 (long long)kMaxRowStride);
   {
     const int64_t rpb = beam::prefill_rows_per_block(L.kind, false);

@@ -22,9 +22,9 @@
 //  * Full layers: 8 waves (2 per SIMD) x 32 rows = 256 rows per workgroup. Sliding
 //    layers: 4 waves x 32 rows, two workgroups per CU, so that one workgroup's start-up
 //    (Q rows, first tile) and end (output) overlap the other's compute -- a sliding row
-//    tile only spans about 9 key tiles. Their rows of q, gate and out also pass through
-//    LDS, so that every global access moves whole rows (see prefill_rows). Per 32-key
-//    half of a tile a wave computes
+//    tile only spans about 9 key tiles. Rows of q, gate and out pass through LDS, so
+//    that every global access moves whole rows (see prefill_rows). Per 32-key half of a
+//    tile a wave computes
 //    S^T = K Q^T with MFMA 32x32x16 bf16 (K from LDS, Q^T held in registers); a lane
 //    then holds 16 scores of one row, so row max/sum take one cross-half swap
 //    (permlane32).
@@ -226,14 +226,18 @@ __device__ __forceinline__ void prefill_rows(
   const int row_pos = row_valid ? first_pos + my_row / L.G : -1;
   const int row_lo = (swa && row_valid) ? max(row_pos - L.window + 1, 0) : 0;
 
-  // Sliding layers: a row tile sees only about nine key tiles, so moving its rows of q,
-  // gate and out is a large share of its time. These go through LDS, so that each global
-  // access instruction moves whole 256-byte rows (4 rows, 1 KiB): Q is copied straight
-  // into the second tile buffer with the first tile, the gate into the free buffer during
-  // the last tile, and the gated output is assembled in place of the gate, then stored
-  // row by row. Each wave moves its own 32 rows, swizzled like the K/V tiles. Row R of
-  // the tile is token t_first + (r0m + R) / G, head g G + (r0m + R) % G.
-  constexpr bool kRowLds = swa && !SPLIT;
+  // Rows of q, gate and out go through LDS, so that each global access instruction moves
+  // whole 256-byte rows (4 rows, 1 KiB) instead of 16 or 8 bytes of 32 rows. A sliding
+  // row tile sees only about nine key tiles, so these moves are a large share of its
+  // time. Q is copied straight into LDS with the first tile, the gate during the last
+  // tile, and the gated output is assembled in place of the gate, then stored row by
+  // row. Each wave moves its own 32 rows, swizzled like the K/V tiles. Row R of the tile
+  // is token t_first + (r0m + R) / G, head g G + (r0m + R) % G. Full layers keep them in
+  // the upper half of the kernel's LDS (otherwise used only by split blocks' second
+  // stream); sliding layers use the second tile buffer for Q and the free buffer of the
+  // last tile for the gate. Split blocks load Q into registers and store from them.
+  constexpr bool kRowLds = !SPLIT;
+  constexpr int kRowRegion = swa ? -1 : 4 * kTileBytes;
   const int t_first = tile_row0 / L.G;
   const int r0m = tile_row0 - t_first * L.G;
   const float inv_g = 1.0f / (float)L.G;
@@ -500,7 +504,7 @@ __device__ __forceinline__ void prefill_rows(
     if constexpr (kRowLds) {
       if (gate != nullptr) {
         gate_buf = to_buf;
-        issue_rows(gate, gate_stride, to_buf * 2 * kTileBytes);
+        issue_rows(gate, gate_stride, swa ? to_buf * 2 * kTileBytes : kRowRegion);
       }
     }
   };
@@ -542,17 +546,18 @@ __device__ __forceinline__ void prefill_rows(
     issue_tile(s_begin, std::integral_constant<int, 0>{});
     store_staged(std::integral_constant<int, 0>{});
   }
-  if constexpr (kRowLds) issue_rows(q, q_stride, 2 * kTileBytes);
+  if constexpr (kRowLds) issue_rows(q, q_stride, swa ? 2 * kTileBytes : kRowRegion);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   if constexpr (kRowLds) {
     // this lane's row of Q from buffer 1, then every wave is done with it before the
     // second tile is copied there
+    constexpr int kQAt = swa ? 2 * kTileBytes : kRowRegion;
 #pragma unroll
     for (int i = 0; i < 8; ++i)
-      qop[i] = *reinterpret_cast<const bf16x8_t*>(lds + 2 * kTileBytes + (32 * rwave + lr) * kRowBytes +
+      qop[i] = *reinterpret_cast<const bf16x8_t*>(lds + kQAt + (32 * rwave + lr) * kRowBytes +
                                                   (((2 * i + half) ^ swz_key(lr)) << 4));
-    __syncthreads();
+    if constexpr (swa) __syncthreads();
   }
   for (int kt = s_begin; kt < min(p_begin, s_stop); ++kt) masked_step(kt, std::false_type{});
   {
@@ -628,7 +633,7 @@ __device__ __forceinline__ void prefill_rows(
     if (!wave_active) return;
     // every tile is done (the last tile's barrier), so both buffers are free; this
     // wave's rows: the gate's, or buffer 0 without a gate
-    const int rows_at = (gate != nullptr ? gate_buf * 2 * kTileBytes : 0) + 32 * rwave * kRowBytes;
+    const int rows_at = (swa ? (gate != nullptr ? gate_buf * 2 * kTileBytes : 0) : kRowRegion) + 32 * rwave * kRowBytes;
     if (row_valid) {
       const float inv = lsum > 0.f ? (fp8 ? C.v_scale : 1.0f) / lsum : 0.f;
       const int h = g * L.G + my_row % L.G;

@@ -98,8 +98,8 @@ int main(void) {
           BEAM_ERR_INVALID_ARG);
   }
 
-  /* sliding-layer prefill moves a row tile's q, gate and out rows through 32-bit
-   * offsets: token strides above 4,194,303 elements are refused before any launch */
+  /* prefill moves a row tile's q, gate and out rows through 32-bit offsets: token
+   * strides above 4,194,303 elements are refused before any launch, for both kinds */
   {
     static uint64_t fake[64];
     static int32_t meta[4];
@@ -125,6 +125,8 @@ int main(void) {
     CHECK(beam_attn_prefill(&swa, &one, &cache, fake, 6144, fake, 4194304, fake, fake + 32, 6144,
                             NULL) == BEAM_ERR_INVALID_ARG);
     CHECK(beam_attn_prefill(&swa, &one, &cache, fake, 6144, NULL, 0, NULL, fake + 32, 4194304,
+                            NULL) == BEAM_ERR_INVALID_ARG);
+    CHECK(beam_attn_prefill(&full, &one, &cache, fake, 4194304, NULL, 0, NULL, fake + 32, 6144,
                             NULL) == BEAM_ERR_INVALID_ARG);
   }
 
