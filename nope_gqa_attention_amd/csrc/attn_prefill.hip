@@ -241,9 +241,12 @@ __device__ __forceinline__ void prefill_rows(
   const int t_first = tile_row0 / L.G;
   const int r0m = tile_row0 - t_first * L.G;
   const float inv_g = 1.0f / (float)L.G;
-  // byte offset of chunk slot (lane % 16) of row 32 rwave + 4 i + lane / 16 in a row
-  // tensor of token stride `stride` (elements), relative to token t_first; past the
-  // tile's rows, an offset outside the buffer range
+  // byte offset of chunk slot (ln % 16) of row 32 rwave + 4 i + ln / 16 in a row tensor
+  // of token stride `stride` (elements), relative to token t_first; past the tile's
+  // rows, an offset outside the buffer range. The entry point bounds the strides at
+  // 4,194,303 elements, so that the farthest row (255 tokens on, when G = 1) stays below
+  // 2^31 bytes. x / G is taken in fp32: x < 2^9, so x + 0.5 over G is at least 0.5 / G
+  // from an integer, far beyond the rounding of the product.
   auto row_off = [&](int i, int64_t stride, int ln) -> uint32_t {
     const int r = 32 * rwave + 4 * i + ln / 16;
     const int x = r0m + r;
@@ -259,6 +262,8 @@ __device__ __forceinline__ void prefill_rows(
   // copy this wave's 32 rows of a row tensor into LDS at `dst` (+ 32 rwave rows)
   auto issue_rows = [&](const uint16_t* base, int64_t stride, int dst) {
     const __amdgpu_buffer_rsrc_t r = row_rsrc(base, stride);
+    // the lane index made opaque, so that the offsets are formed here: the gate's copy
+    // sits inside the tile loops, which would otherwise keep them in registers throughout
     int ln = lane;
     asm volatile("" : "+v"(ln));
 #pragma unroll
