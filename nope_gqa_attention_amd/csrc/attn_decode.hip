@@ -193,8 +193,10 @@ __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(W == kDe
   // This wave's pages: keys pk = k_begin + 64*(wave + W*pi), pi = 0, 1, ...; each page is
   // two half-steps of 32 keys, each loaded into one register set and then computed. The
   // kernel is built for 2-3 resident waves per SIMD, whose loads hide each other's
-  // latency; a second register set per wave would halve that residency.
-  const int64_t first_pk = k_begin + (int64_t)kPage * wave;
+  // latency; a second register set per wave would halve that residency. (The wave index
+  // is read into a scalar register: a per-lane 64-bit first page made the three-block
+  // fp8 kernel spill.)
+  const int64_t first_pk = k_begin + (int64_t)kPage * __builtin_amdgcn_readfirstlane(wave);
   int n_half = 0;
   if (first_pk < k_end) {
     const int64_t n_pages = (k_end - first_pk + kStep - 1) / kStep;
