@@ -60,11 +60,13 @@ int device_cu_count() {
 // registers and LDS), so an XCD's share of the row tiles runs in rounds of one tile per
 // CU. Halving a row tile and giving each half of its key tiles to one of two 4-wave
 // streams gives two workgroups of about 0.58 of the time each (the second stream's own
-// tile copies and the merge cost the rest). Mode 2 splits the tiles of an XCD's last
-// round when that round would leave at least half of its CUs idle: 384 row tiles on 256
-// CUs (2 rounds, the second half empty) run 256 whole tiles, then 256 split halves, and
-// a grid of a few dozen tiles runs all split. Contexts under 1,024 keys keep whole
-// ranges: a workgroup's fixed costs would dominate its half.
+// tile copies and the merge cost the rest). Mode 2 splits as many tiles of an XCD's last
+// round as that round leaves CUs idle: 384 row tiles on 256 CUs (2 rounds, the second
+// half empty) run 256 whole tiles, then 256 split halves; the 192 tiles of a 1,024-token
+// prefill (one round, 64 CUs idle) split their 64 longest (the last 8 of each XCD's 24,
+// causal tiles that see the most keys); a grid of a few dozen tiles runs all split.
+// Contexts under 1,024 keys keep whole ranges: a workgroup's fixed costs would dominate
+// its half.
 // BEAMATTN_PREFILL_KEY_SPLIT=0 (never) or 1 (every row tile) in the environment overrides
 // the choice.
 int choose_prefill_split_mode(const beam::LayerParams& L, const beam::BatchParams& B) {

@@ -134,13 +134,13 @@ __device__ __forceinline__ float swap_halves_sum(float x) {
 // KV head) are consecutive, so that the blocks streaming the same K/V pages share an L2.
 // Full layers may run some units as two blocks of half the rows with the key range split
 // between two wave streams (prefill_rows, SPLIT): split_mode 1 splits every unit; 2 splits
-// the units of an XCD's last round when that round would leave at least half of the XCD's
-// CUs idle (one prefill block runs per CU at a time), so that it runs twice as many
-// blocks of about half the length.
+// as many of the units of an XCD's last round as that round leaves CUs idle (one prefill
+// block runs per CU at a time), the last units of the XCD's range first: those are the
+// later row tiles of a (sequence, KV head), which see the most keys.
 struct PrefillGrid {
   int32_t units;
   int32_t tiles;           // row tiles per (sequence, KV head)
-  int32_t split_mode;      // 0 none, 1 all, 2 the last round where it is at most half full
+  int32_t split_mode;      // 0 none, 1 all, 2 last-round units, up to its idle CUs
   int32_t cus_per_xcd;
 };
 
@@ -156,7 +156,8 @@ __host__ __device__ inline void prefill_xcd_plan(const PrefillGrid& P, int xcd, 
   } else if (P.split_mode == 2 && *n > 0) {
     const int rounds = (*n + P.cus_per_xcd - 1) / P.cus_per_xcd;
     const int last = *n - (rounds - 1) * P.cus_per_xcd;
-    if (2 * last <= P.cus_per_xcd) *n_split = last;
+    const int idle = P.cus_per_xcd - last;
+    *n_split = last < idle ? last : idle;
   }
 }
 

@@ -108,9 +108,9 @@ constexpr int prefill_rows_per_block(int kind, bool key_split) {
   return 32 * (kind == BEAM_LAYER_SWA ? 4 : (key_split ? 4 : 8));
 }
 
-// split_mode: 0 no key split, 1 every row tile split, 2 the row tiles of a last round
-// that would leave at least half of an XCD idle (full layers; sliding ones never split);
-// cus: the device's compute units.
+// split_mode: 0 no key split, 1 every row tile split, 2 as many row tiles of an XCD's last
+// round as it leaves CUs idle (full layers; sliding ones never split); cus: the device's
+// compute units.
 hipError_t launch_attn_prefill(const LayerParams& L, const BatchParams& B, const CacheParams& C,
                                int split_mode, int cus, const void* q, int64_t q_stride,
                                const void* gate, int64_t gate_stride, const void* gate_bias,
