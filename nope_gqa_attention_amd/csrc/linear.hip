@@ -20,6 +20,8 @@
 //    addresses: +4-5% against global_load_lds with 64-bit addresses), double-buffered. gfx950's LDS has 64 four-byte banks, so two 128-byte rows fill them;
 //    the 16-byte chunk c of row r is stored at slot c ^ ((r / 2) mod 8), so the 16 rows a
 //    16-lane group of an operand read touches (one chunk each) cover all 64 banks.
+//  * The output tile goes through LDS as bf16 rows and is stored 512 contiguous bytes per
+//    32 lanes (+2.6% on both projections against 8-byte stores scattered over 32 rows).
 //  * Workgroups are remapped so that each XCD runs a contiguous range of tiles, ordered
 //    4 m-tiles at a time: the ~32 workgroups an XCD runs together cover a 4 x 8 block of
 //    tiles and share each x and W slab through its L2.
@@ -159,22 +161,34 @@ __global__ __launch_bounds__(kLinThreads) void linear_bf16_kernel(
     __syncthreads();
   }
 
-  // ---- epilogue: lane holds D[n][m] for m = its column, n = 4 consecutive values per
-  // register quad; bf16 (RNE) and one 8-byte store per quad
+  // ---- epilogue through LDS (free: the last stage ended with a barrier): the tile as bf16
+  // rows [256 m][256 n], 16-byte chunk c of row m at slot c ^ (m mod 32), then each wave
+  // stores 32 whole rows, 512 contiguous bytes per 32 lanes. A lane holds D[n][m] for m =
+  // its column and 4 consecutive n per register quad.
 #pragma unroll
   for (int mb = 0; mb < 4; ++mb) {
-    const int64_t m = m0 + 128 * wm + 32 * mb + lr;
-    if (m >= M) continue;
+    const int ml = 128 * wm + 32 * mb + lr;
 #pragma unroll
     for (int nb = 0; nb < 2; ++nb)
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4) {
-        const int64_t n = n0 + 64 * wn + 32 * nb + 8 * q4 + 4 * half;
-        if (n >= N) continue;
+        const int c = 8 * wn + 4 * nb + q4;                 // (64 wn + 32 nb + 8 q4) / 8
         const f32x16_t& d = acc[nb][mb];
         const u32x2_t o = {pack_bf16x2(d[4 * q4], d[4 * q4 + 1]), pack_bf16x2(d[4 * q4 + 2], d[4 * q4 + 3])};
-        *reinterpret_cast<u32x2_t*>(y + m * y_stride + n) = o;
+        *reinterpret_cast<u32x2_t*>(lds + ml * 512 + ((c ^ (ml & 31)) << 4) + 8 * half) = o;
       }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int ml = 32 * wave + 2 * i + lane / 32, c = lane % 32;
+    const int64_t m = m0 + ml, n = n0 + 8 * c;
+    if (m < M && n < N) {
+      const u32x4_t v = *reinterpret_cast<const u32x4_t*>(lds + ml * 512 + ((c ^ (ml & 31)) << 4));
+      uint16_t* dst = y + m * y_stride + n;
+      if (n + 8 <= N) *reinterpret_cast<u32x4_t*>(dst) = v;
+      else *reinterpret_cast<u32x2_t*>(dst) = u32x2_t{v[0], v[1]};   // n % 8 == 4 at the end
+    }
   }
 }
 

@@ -67,6 +67,20 @@ def test_linear_strided_views():
     assert torch.all(yb[:, :128] == 7.0) and torch.all(yb[:, 256:] == 7.0)
 
 
+def test_linear_partial_last_chunk_leaves_neighbours_untouched():
+    """n % 8 == 4: the last 16-byte chunk of each output row is half inside the matrix;
+    the columns after it (a wider tensor's) must keep their values."""
+    from nope_gqa_attention_amd import beamattn as ba
+    say("case linear n % 8 == 4")
+    x, w = synth.make_linear(260, 260, 128, [85, 0], device="cuda")
+    yb = torch.full((260, 272), 7.0, dtype=torch.bfloat16, device="cuda")
+    y = yb[:, :260]
+    ba.beam_linear_bf16(x, w, y)
+    torch.cuda.synchronize()
+    _check(x, w, y)
+    assert torch.all(yb[:, 260:] == 7.0)
+
+
 @pytest.mark.parametrize("n,k", [(14336, 5120), (5120, 6144)], ids=["qkv_gate", "o_proj"])
 def test_linear_projection_shapes_at_16k_tokens(n, k):
     from nope_gqa_attention_amd import beamattn as ba
