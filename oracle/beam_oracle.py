@@ -452,7 +452,8 @@ def layer_call(inp: dict, rows=None):
     inp keys: kind, kv_dtype, q_start [B+1], kv_len [B], block_table [B, P],
       q [N,Hq,D] / k [N,Hkv,D] / v [N,Hkv,D] / gate [N,Hq*D] bf16 bits,
       q_norm_w, k_norm_w [D] bf16 bits, gate_bias [Hq] bf16 bits,
-      k_cache, v_cache (bits/codes), k_scale, v_scale.
+      k_cache, v_cache (bits/codes), k_scale, v_scale; optional window (sliding
+      layers' key count, 512 by default).
     rows: optional indices of new tokens whose attention output to compute (all if
       None). Returns dict with q_out bits [N,Hq,D], k_cache, v_cache (after the
       store), o [R,Hq,D] fp64 (ungated), y [R,Hq,D] fp64 (gated), rows.
@@ -470,7 +471,8 @@ def layer_call(inp: dict, rows=None):
     rows = np.asarray(rows, dtype=np.int64)
     fn = attention_rows_long if int(np.max(np.asarray(inp["kv_len"]))) > 65536 else attention_rows
     o = fn(q_out[rows], k_cache, v_cache, inp["block_table"], seq[rows], pos[rows], kind,
-           kv_dtype, inp.get("k_scale", 1.0), inp.get("v_scale", 1.0))
+           kv_dtype, inp.get("k_scale", 1.0), inp.get("v_scale", 1.0),
+           window=int(inp.get("window", WINDOW)))
     y = head_gate(o, np.asarray(inp["gate"])[rows], inp["gate_bias"])
     return {"q_out": q_out, "k_out": k_out, "k_cache": k_cache, "v_cache": v_cache,
             "o": o, "y": y, "rows": rows, "seq": seq, "pos": pos}

@@ -41,6 +41,11 @@ def test_sliding_window_and_causal_visibility_match_transformers_masks():
     assert np.array_equal(ours_full, full)
     # 512 keys per row once the window is full, the query's own key among them
     assert swa[600].sum() == 512 and swa[600, 600] and not swa[600, 88]
+    # other window lengths (the layer descriptor's window is a parameter)
+    for w in (1, 64, 200, 1000):
+        ref = mu.sliding_window_causal_mask_function(w)(0, 0, q, kv).numpy()
+        lo_w = np.array([O.visible_range(int(p), O.KIND_SWA, w)[0] for p in range(1200)])[:, None]
+        assert np.array_equal((kn >= lo_w) & (kn <= qn), ref), w
 
 
 def test_query_heads_read_kv_heads_as_repeat_kv_maps_them():
