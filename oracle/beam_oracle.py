@@ -452,16 +452,21 @@ def layer_call(inp: dict, rows=None):
     inp keys: kind, kv_dtype, q_start [B+1], kv_len [B], block_table [B, P],
       q [N,Hq,D] / k [N,Hkv,D] / v [N,Hkv,D] / gate [N,Hq*D] bf16 bits,
       q_norm_w, k_norm_w [D] bf16 bits, gate_bias [Hq] bf16 bits,
-      k_cache, v_cache (bits/codes), k_scale, v_scale; optional window (sliding
-      layers' key count, 512 by default).
+      k_cache, v_cache (bits/codes), k_scale, v_scale; optional layer constants
+      window, rope_theta, rms_eps, ssmax_base, ssmax_exponent, sm_scale (the model's
+      values by default).
     rows: optional indices of new tokens whose attention output to compute (all if
       None). Returns dict with q_out bits [N,Hq,D], k_cache, v_cache (after the
       store), o [R,Hq,D] fp64 (ungated), y [R,Hq,D] fp64 (gated), rows.
     """
     kind, kv_dtype = inp["kind"], inp["kv_dtype"]
     seq, pos = new_token_positions(inp["q_start"], inp["kv_len"])
-    q_out = prepare_qk(inp["q"], inp["q_norm_w"], pos, kind, True)
-    k_out = prepare_qk(inp["k"], inp["k_norm_w"], pos, kind, False)
+    consts = {"theta": float(inp.get("rope_theta", ROPE_THETA)),
+              "eps": float(inp.get("rms_eps", RMS_EPS)),
+              "ssmax_base": float(inp.get("ssmax_base", SSMAX_BASE)),
+              "ssmax_exponent": float(inp.get("ssmax_exponent", SSMAX_EXPONENT))}
+    q_out = prepare_qk(inp["q"], inp["q_norm_w"], pos, kind, True, **consts)
+    k_out = prepare_qk(inp["k"], inp["k_norm_w"], pos, kind, False, **consts)
     k_cache = store_kv(inp["k_cache"], inp["block_table"], seq, pos, k_out, kv_dtype,
                        inp.get("k_scale", 1.0))
     v_cache = store_kv(inp["v_cache"], inp["block_table"], seq, pos, inp["v"], kv_dtype,
@@ -472,7 +477,7 @@ def layer_call(inp: dict, rows=None):
     fn = attention_rows_long if int(np.max(np.asarray(inp["kv_len"]))) > 65536 else attention_rows
     o = fn(q_out[rows], k_cache, v_cache, inp["block_table"], seq[rows], pos[rows], kind,
            kv_dtype, inp.get("k_scale", 1.0), inp.get("v_scale", 1.0),
-           window=int(inp.get("window", WINDOW)))
+           sm_scale=float(inp.get("sm_scale", SM_SCALE)), window=int(inp.get("window", WINDOW)))
     y = head_gate(o, np.asarray(inp["gate"])[rows], inp["gate_bias"])
     return {"q_out": q_out, "k_out": k_out, "k_cache": k_cache, "v_cache": v_cache,
             "o": o, "y": y, "rows": rows, "seq": seq, "pos": pos}
