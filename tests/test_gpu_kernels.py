@@ -210,6 +210,22 @@ def test_ungated_attention_then_standalone_gate_equals_fused():
     assert np.abs(a - b).max() <= 2e-2
 
 
+@pytest.mark.parametrize("kind", ["swa", "full"])
+@pytest.mark.parametrize("mode", ["prefill", "decode"])
+@pytest.mark.parametrize("kv_dtype", ["bf16", "fp8"])
+def test_ungated_attention_matches_oracle(kind, mode, kv_dtype):
+    """gate = NULL: the attention output itself, o[t,h] of the oracle (no sigmoid)."""
+    say(f"case ungated kind={kind} mode={mode} dtype={kv_dtype}")
+    q_lens = [300, 77, 5] if mode == "prefill" else [1, 7, 16]
+    call = synth.make_call(q_lens, [1500, 77, 700], kind, kv_dtype, [28, len(kind), len(mode)])
+    ref = O.layer_call(call.oracle_inputs())["o"]
+    d = stage(call)
+    run_kvwrite(d)
+    run_attend(d, mode=mode, gate=False)
+    torch.cuda.synchronize()
+    assert_close_to_oracle(bits16(d["out"]), ref, kv_dtype, f"ungated {kind} {mode} {kv_dtype}")
+
+
 # ------------------------------------------------------------------ ABI errors launch nothing
 
 def test_invalid_arguments_return_status_and_launch_nothing():
