@@ -604,7 +604,7 @@ def main():
         return
     if args.gpus != 1:
         print(f"bench.py runs on exactly one GPU; --gpus {args.gpus} is not supported "
-              "(this build has no multi-GPU path)", file=sys.stderr)
+              "(libbeamattn has no multi-GPU path)", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
