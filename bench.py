@@ -577,7 +577,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-rows", type=int, default=64,
+    ap.add_argument("--cpu-rows", type=int, default=256,
                     help="oracle rows sampled per sequence of the long prefill")
     ap.add_argument("--only", choices=("all", "prefill", "decode"), default="all",
                     help="restrict the run (for counter collection); the JSON line needs 'all'")
