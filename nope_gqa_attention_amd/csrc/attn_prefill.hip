@@ -561,8 +561,8 @@ __device__ __forceinline__ void prefill_rows(
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   if constexpr (kRowLds) {
-    // this lane's row of Q from buffer 1, then every wave is done with it before the
-    // second tile is copied there
+    // this lane's row of Q; sliding layers then make sure every wave is done with buffer
+    // 1 before the second tile is copied there
     constexpr int kQAt = swa ? 2 * kTileBytes : kRowRegion;
 #pragma unroll
     for (int i = 0; i < 8; ++i)
@@ -642,8 +642,9 @@ __device__ __forceinline__ void prefill_rows(
   const float lsum = swap_halves_sum(l_run);
   if constexpr (kRowLds) {
     if (!wave_active) return;
-    // every tile is done (the last tile's barrier), so both buffers are free; this
-    // wave's rows: the gate's, or buffer 0 without a gate
+    // every tile is done (the last tile's barrier), so the tile buffers are free; this
+    // wave's rows: full layers' upper LDS half, or (sliding) the gate's buffer, or buffer
+    // 0 without a gate
     const int rows_at = (swa ? (gate != nullptr ? gate_buf * 2 * kTileBytes : 0) : kRowRegion) + 32 * rwave * kRowBytes;
     if (row_valid) {
       const float inv = lsum > 0.f ? (fp8 ? C.v_scale : 1.0f) / lsum : 0.f;
