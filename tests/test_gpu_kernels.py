@@ -148,6 +148,7 @@ DECODE_CASES = [
     ("q3", [3, 3, 2], [3, 2000, 6000]),
     ("q8-split", [8], [20000]),
     ("q16", [16, 5], [16, 4100]),
+    ("finished-seqs", [0, 2, 0, 1], [700, 3000, 64, 9000]),   # sequences with no new token
 ]
 
 
